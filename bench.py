@@ -1,0 +1,238 @@
+#!/usr/bin/env python
+"""Throughput of the Mixtral sparse-MoE layer on one MI355X.
+
+A step is one whole layer (router, dispatch, the two expert GEMMs, combine)
+over one batch of the workload's synthetic tokens, inputs resident in HBM.
+For the stack workload a step is all of its h + moe(rms_norm(h)) blocks.
+
+Prints one JSON line.  `roofline` covers the dominant kernel (the W1/W3
+GEMM with the SwiGLU epilogue), timed live with HIP events recorded by the
+library on the launch stream around that kernel in every timed step.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload (rank 0, one GPU only).
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|stack|tiny]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s (d4096,ff14336,E8,k2); %MFMA peak prefill, %HBM BW decode"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime (the library records them)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                          ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, e: int):
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def gemm1_work(w, counts):
+    """Algorithmic work of the W1/W3 + SwiGLU GEMM for one launch.
+
+    bytes: W1 and W3 rows of every expert that received tokens (2*d_ff*d
+    elements each), the A = T*k gathered token rows (d elements each) and
+    the A SwiGLU rows written (d_ff elements each).
+    flops: 2 multiply-adds' worth per weight per assignment: 2 * A * d * 2*d_ff.
+    """
+    es = 4 if w.dtype == "f32" else 2
+    A = w.T * w.k
+    n_active = int((counts > 0).sum())
+    nbytes = n_active * 2 * w.d_ff * w.d * es + A * w.d * es + A * w.d_ff * es
+    flops = 2 * A * w.d * 2 * w.d_ff
+    return nbytes, flops, n_active
+
+
+def layer_work(w, n_active):
+    """Whole-layer algorithmic work: FLOPs = T(2*k*3*d*d_ff + 2*d*E); bytes =
+    active experts' weights + x read + y written + the fp32 gate matrix."""
+    es = 4 if w.dtype == "f32" else 2
+    flops = w.T * (2 * w.k * 3 * w.d * w.d_ff + 2 * w.d * w.E)
+    nbytes = n_active * 3 * w.d * w.d_ff * es + 2 * w.T * w.d * es + w.E * w.d * 4
+    return nbytes, flops
+
+
+def cpu_baseline(w, L, budget_tokens):
+    """The oracle, as it stands, on a bounded token sample of the same layer."""
+    import numpy as np
+
+    import oracle
+
+    rows = np.arange(min(w.T, budget_tokens), dtype=np.int64)
+    host = {n: L[n].cpu() for n in ("x", "Wg", "W1", "W3", "W2")}
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.moe_rows(host["x"], host["Wg"], host["W1"], host["W3"], host["W2"], w.k, rows=rows,
+                    nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {len(rows)} of the {w.T} tokens of the {w.name} workload "
+                      f"(tokens are independent), {dt:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "prefill", "skewed", "stack"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="oracle sample size (default sized to ~10-30 s)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs the layer on one GPU only; --gpus {args.gpus} / WORLD_SIZE {world} "
+              "is not supported (the layer has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_31_amd import moe
+    from sparse_mixture_experts_31_amd.inputs import WORKLOADS, make_layer, make_stack
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name}: T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} k={w.k} "
+          f"{w.dtype} blocks={w.blocks}", file=sys.stderr, flush=True)
+    ev = HipEvents()
+    stream = torch.cuda.current_stream()
+
+    if w.blocks > 1:
+        h0, blocks = make_stack(w, dev, args.seed)
+        L = dict(x=h0, **blocks[0])
+    else:
+        L = make_layer(w, dev, args.seed)
+        blocks = None
+    torch.cuda.synchronize()
+    print("[bench] inputs ready", file=sys.stderr, flush=True)
+
+    ws = moe.workspace(w.T, w.d, w.d_ff, w.E, w.k, L["x"].dtype, dev)
+    y = torch.empty_like(L["x"])
+    eps = float(np.float32(w.eps))
+
+    def step(marks):
+        if blocks is None:
+            moe.moe_forward_profiled(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.k, marks,
+                                     y=y, ws=ws, stream=stream)
+        else:
+            h = y
+            h.copy_(L["x"])
+            for B in blocks:
+                moe.moe_block_forward(h, B["Wg"], B["W1"], B["W3"], B["W2"], w.k, eps, ws=ws,
+                                      stream=stream)
+
+    none6 = [None] * 6
+    for _ in range(args.warmup):
+        step(none6)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step([None, None, pairs[i][0], pairs[i][1], None, None] if blocks is None else none6)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / (t1 - t0)
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr,
+          flush=True)
+
+    # routing of this batch (for the active-expert count of the byte model)
+    idx, _ = moe.moe_route(L["x"], L["Wg"], w.k)
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.E)
+    g_bytes, g_flops, n_active = gemm1_work(w, counts)
+    l_bytes, l_flops = layer_work(w, n_active)
+
+    roofline = None
+    if blocks is None:
+        gemm1_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+        if w.T * w.k < 64 * w.E:       # weight streaming: HBM-bound
+            achieved = g_bytes / (gemm1_ms * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                        "traffic": None}
+        else:
+            peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+            achieved = g_flops / (gemm1_ms * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+        roofline["kernel"] = "grouped_gemm_kernel<SWIGLU> (W1/W3 + silu*v)"
+        roofline["kernel_ms"] = round(gemm1_ms, 4)
+        roofline["alg_bytes"] = g_bytes
+        roofline["alg_flops"] = g_flops
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    step_s = ms_per_step * 1e-3
+    nblk = max(1, w.blocks)
+    layer = {"alg_bytes": l_bytes * nblk, "alg_flops": l_flops * nblk,
+             "hbm_frac": round(l_bytes * nblk / step_s / 1e9 / PEAK_HBM_GBS, 4),
+             "mfma_frac": round(l_flops * nblk / step_s / 1e12 /
+                                (PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS), 4),
+             "active_experts": n_active}
+
+    cpu = None
+    if not args.no_cpu_baseline and blocks is None:
+        budget = args.cpu_tokens or max(8, min(w.T, 48))
+        print(f"[bench] oracle baseline on {budget} tokens", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, L, budget)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
+                   "blocks": w.blocks, "act_dtype": w.dtype, "router_dtype": "f32",
+                   "seed": args.seed},
+        "roofline": roofline, "cpu_baseline": cpu, "layer_roofline": layer,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -49,6 +49,8 @@ def lib():
         L.orc_moe_rows.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32, P, i64,
                                    P, P, P, P, P, i32]
         L.orc_rmsnorm.argtypes = [P, i32, dbl, P]
+        L.orc_rmsnorm_rows.argtypes = [P, i64, i32, dbl, i32, P]
+        L.orc_rmsnorm_rows.restype = ctypes.c_int
         L.orc_block_step.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, dbl, P, P, P, P,
                                      i32]
         for name in ("orc_router_logits", "orc_topk_gates", "orc_permute", "orc_swiglu_expert",
@@ -191,6 +193,16 @@ def rmsnorm(h, eps):
     ha = np.ascontiguousarray(h, np.float64)
     out = np.empty_like(ha)
     _check(lib().orc_rmsnorm(_ptr(ha), ha.shape[0], float(eps), _ptr(out)), "rmsnorm")
+    return out
+
+
+def rmsnorm_rows(h, eps, round_bf16=True):
+    """rmsnorm of every row of h (f64[n][d]), optionally rounded to bf16."""
+    ha = np.ascontiguousarray(h, np.float64)
+    n, d = ha.shape
+    out = np.empty_like(ha)
+    _check(lib().orc_rmsnorm_rows(_ptr(ha), n, d, float(eps), int(bool(round_bf16)), _ptr(out)),
+           "rmsnorm_rows")
     return out
 
 

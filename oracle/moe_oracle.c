@@ -335,6 +335,16 @@ int orc_rmsnorm(const double *h, int d, double eps, double *out) {
     return 0;
 }
 
+int orc_rmsnorm_rows(const double *h, long n, int d, double eps, int round_bf16, double *out) {
+    if (n < 0 || d < 1 || (n > 0 && (!h || !out))) return -1;
+    for (long r = 0; r < n; ++r) {
+        orc_rmsnorm(h + (size_t)r * d, d, eps, out + (size_t)r * d);
+        if (round_bf16)
+            for (int i = 0; i < d; ++i) out[(size_t)r * d + i] = orc_bf16_round(out[(size_t)r * d + i]);
+    }
+    return 0;
+}
+
 typedef struct {
     double *h;
     const float *Wg;

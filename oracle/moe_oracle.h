@@ -75,6 +75,10 @@ int orc_moe_rows(const void *x, int x_dt, const float *Wg, const void *W1,
 /* RMSNorm with unit gain: out_i = h_i / sqrt(mean(h^2) + eps), fp64. */
 int orc_rmsnorm(const double *h, int d, double eps, double *out);
 
+/* rmsnorm of each of n rows of h[n][d]; with round_bf16 != 0 each output is
+ * rounded to the nearest bf16 value (the activations the router then sees). */
+int orc_rmsnorm_rows(const double *h, long n, int d, double eps, int round_bf16, double *out);
+
 /* One decoder-block MoE step on n independent rows held as bf16 values in
  * fp64 (h[n][d], updated in place):
  *     xn = bf16(rmsnorm(h));  h <- bf16(h + moe(xn)).

@@ -1,0 +1,81 @@
+// common.h — device helpers and launcher declarations shared by the HIP
+// sources of libmoe.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Element types: fp32 or bf16 held as raw 16-bit patterns.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// fp64 -> bf16, one rounding to nearest even straight from the double (no
+// intermediate fp32 rounding).  bf16 keeps 7 explicit mantissa bits, so the
+// rounding point of a normal double sits at mantissa bit 45.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double v) {
+    uint64_t u = (uint64_t)__double_as_longlong(v);
+    uint64_t sign = u >> 63;
+    uint64_t mag = u & 0x7fffffffffffffffull;
+    if (mag >= 0x7ff0000000000000ull)  // Inf / NaN: the fp32 conversion keeps them
+        return f32_to_bf16_bits((float)v);
+    double a = __longlong_as_double((long long)mag);
+    float f;
+    if (a < 0x1p-126) {
+        // below the fp32 normal range bf16 steps are 2^-133 apart
+        f = (float)(rint(a * 0x1p133) * 0x1p-133);
+    } else {
+        uint64_t lsb = (mag >> 45) & 1ull;
+        mag += 0x00000fffffffffffull + lsb;
+        mag &= ~0x00001fffffffffffull;
+        double r = __longlong_as_double((long long)mag);
+        f = (r >= 0x1p128) ? __builtin_inff() : (float)r;  // exact when finite
+    }
+    return (__float_as_uint(f) >> 16) | (uint32_t)(sign << 15);
+}
+
+}  // namespace moe
+
+// ---- launchers (host side, one per kernel family) -------------------------
+
+hipError_t moe_launch_router(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
+                             int k, int32_t *idx, float *gw, float *logits, hipStream_t s);
+hipError_t moe_launch_dispatch_index(const int32_t *idx, int64_t A, int E, int k,
+                                     int32_t *counts, int32_t *offsets, int32_t *row_of,
+                                     int32_t *token_of, hipStream_t s);
+hipError_t moe_launch_gather_rows(const void *x, int dt, int64_t T, int d, int k,
+                                  const int32_t *row_of, void *x_perm, hipStream_t s);
+// Grouped expert GEMMs.  `gather` (may be NULL) maps a row of an expert's
+// block to the activation row it reads (token_of); NULL means the activation
+// is already in expert order (x_perm).  `mid_event` (may be NULL) is recorded
+// between the W1/W3 GEMM and the W2 GEMM.
+hipError_t moe_launch_expert_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
+                                 const void *W1, const void *W3, const void *W2, int dt,
+                                 int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
+                                 hipEvent_t mid_event, hipStream_t s);
+hipError_t moe_launch_combine(const void *out_perm, const int32_t *row_of, const float *gw,
+                              const void *residual, int dt, int64_t T, int d, int k, void *y,
+                              hipStream_t s);
+hipError_t moe_launch_rmsnorm(const void *h, int dt, int64_t T, int d, float eps, void *out,
+                              hipStream_t s);

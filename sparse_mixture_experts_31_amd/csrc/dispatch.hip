@@ -1,0 +1,134 @@
+// dispatch.hip — group the T*k (token, slot) assignments by expert.
+//
+// Tokens go to the experts they chose, experts can receive none, and an
+// expert with a zero gate is skipped entirely (tokentrails lineage, step
+// "Two experts per token"; flashpapers summary, "How It Works").  Grouping the
+// assignments per expert turns the experts into one grouped GEMM over
+// contiguous row blocks.
+//
+// dispatch_index_kernel (one workgroup of 1024 threads):
+//   1. per-expert histogram with LDS integer atomics (order-free, exact);
+//   2. exclusive scan of the E counts -> offsets;
+//   3. stable ranks, 1024 assignments per round: inside a wave the lanes that
+//      share an expert are found with ballots (one ballot per distinct expert
+//      present in the wave), a lane's rank is the popcount of the matching
+//      lower lanes, and per-wave totals are prefix-summed across the 16 waves
+//      and carried into the next round.  Rows inside an expert's block thus
+//      follow ascending assignment index (t*k + j): a unique, deterministic
+//      order.
+// gather_rows_kernel: one wave per token reads the token's row once with
+//   16-byte loads and writes it to each of its k rows of x_perm.
+#include "common.h"
+
+namespace moe {
+
+constexpr int kDispatchThreads = 1024;
+constexpr int kDispatchWaves = kDispatchThreads / kWave;
+
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_index_kernel(
+    const int32_t *__restrict__ idx, int A, int E, int k, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ row_of, int32_t *__restrict__ token_of) {
+    __shared__ int s_cnt[64];
+    __shared__ int s_base[64];
+    __shared__ int s_wave[kDispatchWaves][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+
+    if (tid < 64) s_cnt[tid] = 0;
+    __syncthreads();
+    for (int a = tid; a < A; a += kDispatchThreads) {
+        const int e = idx[a];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            s_base[e] = run;
+            offsets[e] = run;
+            counts[e] = s_cnt[e];
+            run += s_cnt[e];
+        }
+        offsets[E] = run;
+    }
+    __syncthreads();
+
+    const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int r0 = 0; r0 < A; r0 += kDispatchThreads) {
+        const int a = r0 + tid;
+        const int e = (a < A) ? idx[a] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        s_wave[wave][lane] = 0;
+        __syncthreads();
+        uint64_t rem = __ballot(valid);
+        int rank = 0;
+        while (rem) {
+            const int leader = __ffsll((unsigned long long)rem) - 1;
+            const int le = __shfl(e, leader);
+            const uint64_t m = __ballot(e == le);
+            if (e == le) rank = __popcll(m & lower_lanes);
+            if (lane == leader) s_wave[wave][le] = __popcll(m);
+            rem &= ~m;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int run = s_base[tid];
+            for (int w = 0; w < kDispatchWaves; ++w) {
+                const int c = s_wave[w][tid];
+                s_wave[w][tid] = run;
+                run += c;
+            }
+            s_base[tid] = run;
+        }
+        __syncthreads();
+        if (valid) {
+            const int row = s_wave[wave][e] + rank;
+            row_of[a] = row;
+            token_of[row] = a / k;
+        } else if (a < A) {
+            row_of[a] = -1;
+        }
+        __syncthreads();
+    }
+}
+
+constexpr int kGatherWaves = 4;
+
+__global__ __launch_bounds__(kGatherWaves * kWave) void gather_rows_kernel(
+    const uint4 *__restrict__ x, int64_t T, int row_chunks, int k,
+    const int32_t *__restrict__ row_of, uint4 *__restrict__ x_perm) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = (int64_t)blockIdx.x * kGatherWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    int rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rows[j] = (j < k) ? row_of[t * k + j] : -1;
+    const uint4 *src = x + t * row_chunks;
+    for (int c = lane; c < row_chunks; c += kWave) {
+        const uint4 v = src[c];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (rows[j] >= 0) x_perm[(int64_t)rows[j] * row_chunks + c] = v;
+    }
+}
+
+}  // namespace moe
+
+hipError_t moe_launch_dispatch_index(const int32_t *idx, int64_t A, int E, int k,
+                                     int32_t *counts, int32_t *offsets, int32_t *row_of,
+                                     int32_t *token_of, hipStream_t s) {
+    hipLaunchKernelGGL(moe::dispatch_index_kernel, dim3(1), dim3(moe::kDispatchThreads), 0, s,
+                       idx, (int)A, E, k, counts, offsets, row_of, token_of);
+    return hipGetLastError();
+}
+
+hipError_t moe_launch_gather_rows(const void *x, int dt, int64_t T, int d, int k,
+                                  const int32_t *row_of, void *x_perm, hipStream_t s) {
+    const int es = (dt == 0) ? 4 : 2;
+    const int row_chunks = d * es / 16;
+    const dim3 grid((unsigned)((T + moe::kGatherWaves - 1) / moe::kGatherWaves));
+    hipLaunchKernelGGL(moe::gather_rows_kernel, grid, dim3(moe::kGatherWaves * moe::kWave), 0, s,
+                       (const uint4 *)x, T, row_chunks, k, row_of, (uint4 *)x_perm);
+    return hipGetLastError();
+}

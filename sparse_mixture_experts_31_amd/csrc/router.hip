@@ -1,0 +1,190 @@
+// router.hip — router scores fused with top-k and the softmax over the kept
+// scores.
+//
+// The router is a linear map from a token's vector to one score per expert
+// (ennepo lecture, router passage; tokentrails lineage, step "The router").
+// TopK keeps the k best scores and the softmax runs over them alone
+// (flashpapers summary, "How It Works").
+//
+// One wavefront owns TPW tokens and treats the experts EG at a time.  Each
+// lane walks its strided share of d, 8 elements per step, and accumulates x_i * Wg_e,i in fp64: a bf16 or fp32
+// element times an fp32 weight is exact in fp64, so only the fp64 additions
+// round and the final fp32 score is (almost always) the correctly rounded
+// value of the exact dot product.  That keeps the discrete top-k choice
+// stable against reduction order.  A recursive-halving butterfly reduces the
+// TPW*EG partial sums across the wave with TPW*EG fp64 shuffles instead of
+// TPW*EG*6.  The fp32 scores land in LDS; lane t < TPW
+// then picks the top k of token t (strict '>' over ascending expert index, so
+// equal fp32 scores go to the lower index) and the gates
+// g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+#include "common.h"
+
+namespace moe {
+
+template <typename Tin>
+__device__ __forceinline__ void load8(const Tin *p, float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, float (&v)[8]) {
+    float4 a = *(const float4 *)p;
+    float4 b = *(const float4 *)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t *p, float (&v)[8]) {
+    uint4 a = *(const uint4 *)p;
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+// Sum NV per-lane values across the 64 lanes.  After the call lane L holds
+// the full sum of value index (L / (64 / NV)) in v[0].
+template <int NV>
+__device__ __forceinline__ void wave_reduce_halving(double (&v)[NV], int lane) {
+    int off = 32;
+#pragma unroll
+    for (int cnt = NV; cnt > 1; cnt >>= 1, off >>= 1) {
+        const int half = cnt / 2;
+        const bool hi = (lane & off) != 0;
+#pragma unroll
+        for (int j = 0; j < half; ++j) {
+            double send = hi ? v[j] : v[j + half];
+            double keep = hi ? v[j + half] : v[j];
+            v[j] = keep + __shfl_xor(send, off);
+        }
+    }
+#pragma unroll
+    for (; off >= 1; off >>= 1) v[0] += __shfl_xor(v[0], off);
+}
+
+constexpr int kRouterWaves = 4;
+
+template <typename Tin, int TPW, int EG>
+__global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
+    const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,
+    int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits) {
+    __shared__ float s_logit[kRouterWaves][TPW][64];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t tok0 = ((int64_t)blockIdx.x * kRouterWaves + wave) * TPW;
+
+    for (int e0 = 0; e0 < E; e0 += EG) {
+        double acc[TPW * EG];
+#pragma unroll
+        for (int i = 0; i < TPW * EG; ++i) acc[i] = 0.0;
+        for (int i = lane * 8; i < d; i += kWave * 8) {
+            float xv[TPW][8];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                if (tok0 + t < T) {
+                    load8<Tin>(x + (tok0 + t) * (int64_t)d + i, xv[t]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) xv[t][c] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < EG; ++j) {
+                if (e0 + j < E) {
+                    float wv[8];
+                    load8<float>(Wg + (int64_t)(e0 + j) * d + i, wv);
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                        for (int c = 0; c < 8; ++c)
+                            acc[t * EG + j] = fma((double)xv[t][c], (double)wv[c], acc[t * EG + j]);
+                }
+            }
+        }
+        wave_reduce_halving<TPW * EG>(acc, lane);
+        constexpr int lanes_per_value = 64 / (TPW * EG);
+        if ((lane % lanes_per_value) == 0) {
+            const int vi = lane / lanes_per_value;
+            const int t = vi / EG, j = vi % EG;
+            if (e0 + j < E) s_logit[wave][t][e0 + j] = (float)acc[0];
+        }
+    }
+    __syncthreads();
+
+    // scores out (optional), coalesced over the wave's TPW x E block
+    if (out_logits) {
+        for (int q = lane; q < TPW * E; q += kWave) {
+            const int t = q / E, e = q % E;
+            if (tok0 + t < T) out_logits[(tok0 + t) * E + e] = s_logit[wave][t][e];
+        }
+    }
+    if (lane < TPW && tok0 + lane < T) {
+        const int t = lane;
+        const float *L = s_logit[wave][t];
+        uint64_t used = 0;
+        int sel[8];
+        float sl[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            sel[j] = 0;
+            sl[j] = 0.f;
+            if (j < k) {
+                int best = -1;
+                float bv = 0.f;
+                for (int e = 0; e < E; ++e) {
+                    if ((used >> e) & 1ull) continue;
+                    const float v = L[e];
+                    if (best < 0 || v > bv) {
+                        best = e;
+                        bv = v;
+                    }
+                }
+                used |= 1ull << best;
+                sel[j] = best;
+                sl[j] = bv;
+            }
+        }
+        float z = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k) z += expf(sl[j] - sl[0]);
+        const int64_t o = (tok0 + t) * k;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < k) {
+                out_idx[o + j] = sel[j];
+                out_w[o + j] = expf(sl[j] - sl[0]) / z;
+            }
+        }
+    }
+}
+
+}  // namespace moe
+
+hipError_t moe_launch_router(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
+                             int k, int32_t *idx, float *gw, float *logits, hipStream_t s) {
+    using namespace moe;
+    // Few tokens: one token per wave spreads the row reads over more waves.
+    // Many tokens: four per wave so each gate-weight load serves four rows.
+    const int tpw = (T <= 2048) ? 1 : 4;
+    const int64_t per_block = (int64_t)kRouterWaves * tpw;
+    const dim3 grid((unsigned)((T + per_block - 1) / per_block));
+    const dim3 block(kRouterWaves * kWave);
+    if (dt == 0) {
+        if (tpw == 1)
+            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8>), grid, block, 0, s,
+                               (const float *)x, Wg, T, d, E, k, idx, gw, logits);
+        else
+            hipLaunchKernelGGL((router_topk_kernel<float, 4, 4>), grid, block, 0, s,
+                               (const float *)x, Wg, T, d, E, k, idx, gw, logits);
+    } else {
+        if (tpw == 1)
+            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8>), grid, block, 0, s,
+                               (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits);
+        else
+            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 4, 4>), grid, block, 0, s,
+                               (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits);
+    }
+    return hipGetLastError();
+}

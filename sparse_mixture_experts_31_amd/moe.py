@@ -1,0 +1,204 @@
+"""Thin Python binding over libmoe.so (C ABI declared in include/moe.h).
+
+Every function has the name of the C entry point it wraps and does argument
+marshalling only: it takes torch tensors on the GPU, allocates missing
+outputs with torch, and passes raw device pointers plus the current HIP
+stream to the library.  All arithmetic runs in the library's HIP kernels; if
+libmoe.so is not built, every call raises instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}: {detail}")
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m sparse_mixture_experts_31_amd.build` "
+                "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                ctypes.c_size_t)
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [i32]
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_workspace_size.restype = sz
+        L.moe_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+        sigs = {
+            "moe_route": [P, P, i32, i64, i32, i32, i32, P, P, P, P],
+            "moe_permute": [P, P, i32, i64, i32, i32, i32, P, P, P, P, P, P, sz, P],
+            "moe_expert_ffn": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, sz, P],
+            "moe_combine": [P, P, P, P, i32, i64, i32, i32, P, P],
+            "moe_forward": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, sz, P],
+            "moe_forward_profiled": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, sz, P, P],
+            "moe_rmsnorm": [P, i32, i64, i32, f32, P, P],
+            "moe_block_forward": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, f32, P, P, P, sz,
+                                  P],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = i32
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().moe_status_string(int(s)).decode()
+
+
+def _call(name, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != MOE_OK:
+        raise MoeError(rc, name, lib().moe_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"activations and expert weights must be fp32 or bf16, got {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmoe must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def moe_workspace_size(T, d, d_ff, E, k, dtype) -> int:
+    dt = MOE_F32 if dtype in (torch.float32, MOE_F32) else MOE_BF16
+    return int(lib().moe_workspace_size(T, d, d_ff, E, k, dt))
+
+
+def workspace(T, d, d_ff, E, k, dtype, device="cuda") -> torch.Tensor:
+    n = moe_workspace_size(T, d, d_ff, E, k, dtype)
+    if n == 0:
+        raise ValueError("shape rejected by libmoe")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_route(x, Wg, k, topk_idx=None, topk_w=None, logits=None, stream=None):
+    T, d = x.shape
+    E = Wg.shape[0]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _call("moe_route", _p(x), _p(Wg), _dt(x), T, d, E, k, _p(topk_idx), _p(topk_w), _p(logits),
+          _s(stream))
+    return topk_idx, topk_w
+
+
+def moe_permute(x, topk_idx, E, counts=None, offsets=None, row_of=None, token_of=None,
+                x_perm=None, stream=None):
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
+    token_of = torch.empty(T * k, dtype=torch.int32, device=dev) if token_of is None else token_of
+    x_perm = torch.empty((T * k, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    _call("moe_permute", _p(x), _p(topk_idx), _dt(x), T, d, E, k, _p(counts), _p(offsets),
+          _p(row_of), _p(token_of), _p(x_perm), None, 0, _s(stream))
+    return dict(counts=counts, offsets=offsets, row_of=row_of, token_of=token_of, x_perm=x_perm)
+
+
+def moe_expert_ffn(x_perm, offsets, W1, W3, W2, T, k, out_perm=None, ws=None, stream=None):
+    E, d_ff, d = W1.shape
+    if out_perm is None:
+        out_perm = torch.empty((T * k, d), dtype=x_perm.dtype, device=x_perm.device)
+    if ws is None:
+        ws = workspace(T, d, d_ff, E, k, x_perm.dtype, x_perm.device)
+    _call("moe_expert_ffn", _p(x_perm), _p(offsets), _p(W1), _p(W3), _p(W2), _dt(x_perm), T, d,
+          d_ff, E, k, _p(out_perm), _p(ws), ws.numel(), _s(stream))
+    return out_perm
+
+
+def moe_combine(out_perm, row_of, topk_w, residual=None, y=None, stream=None):
+    T, k = row_of.shape
+    d = out_perm.shape[1]
+    if y is None:
+        y = torch.empty((T, d), dtype=out_perm.dtype, device=out_perm.device)
+    _call("moe_combine", _p(out_perm), _p(row_of), _p(topk_w), _p(residual), _dt(out_perm), T,
+          d, k, _p(y), _s(stream))
+    return y
+
+
+def moe_forward(x, Wg, W1, W3, W2, k, y=None, ws=None, stream=None):
+    T, d = x.shape
+    E, d_ff, _ = W1.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws = workspace(T, d, d_ff, E, k, x.dtype, x.device)
+    _call("moe_forward", _p(x), _p(Wg), _p(W1), _p(W3), _p(W2), _dt(x), T, d, d_ff, E, k, _p(y),
+          _p(ws), ws.numel(), _s(stream))
+    return y
+
+
+def moe_forward_profiled(x, Wg, W1, W3, W2, k, events, y=None, ws=None, stream=None):
+    """moe_forward that records 6 caller-owned hipEvent_t handles (ints or
+    None) around its stages: router, dispatch, GEMM1, GEMM2, combine."""
+    T, d = x.shape
+    E, d_ff, _ = W1.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws = workspace(T, d, d_ff, E, k, x.dtype, x.device)
+    arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e) if e else None for e in events])
+    _call("moe_forward_profiled", _p(x), _p(Wg), _p(W1), _p(W3), _p(W2), _dt(x), T, d, d_ff, E,
+          k, _p(y), _p(ws), ws.numel(), arr, _s(stream))
+    return y
+
+
+def moe_rmsnorm(h, eps, out=None, stream=None):
+    T, d = h.shape
+    if out is None:
+        out = torch.empty_like(h)
+    _call("moe_rmsnorm", _p(h), _dt(h), T, d, float(eps), _p(out), _s(stream))
+    return out
+
+
+def moe_block_forward(h, Wg, W1, W3, W2, k, eps, topk_idx=None, topk_w=None, ws=None,
+                      stream=None):
+    """In place: h <- h + moe(rms_norm(h)).  Returns h."""
+    T, d = h.shape
+    E, d_ff, _ = W1.shape
+    if ws is None:
+        ws = workspace(T, d, d_ff, E, k, h.dtype, h.device)
+    _call("moe_block_forward", _p(h), _p(Wg), _p(W1), _p(W3), _p(W2), _dt(h), T, d, d_ff, E, k,
+          float(eps), _p(topk_idx), _p(topk_w), _p(ws), ws.numel(), _s(stream))
+    return h

@@ -1,0 +1,109 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/moe.h declares, and rejects bad arguments with status codes before
+anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_31_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: checks fail first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+                 "moe_workspace_size", "moe_rmsnorm", "moe_block_forward",
+                 "moe_status_string", "moe_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert moe.status_string(moe.MOE_OK) == "MOE_OK"
+    assert moe.status_string(moe.MOE_ERR_WORKSPACE) == "MOE_ERR_WORKSPACE"
+    assert moe.status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def test_workspace_size_rules():
+    ws = moe.moe_workspace_size
+    base = ws(4096, 4096, 14336, 8, 2, moe.MOE_BF16)
+    assert base > 0
+    # the SwiGLU intermediate dominates: T*k rows of d_ff
+    assert base >= 4096 * 2 * 14336 * 2
+    assert ws(4097, 4096, 14336, 8, 2, moe.MOE_BF16) > base
+    assert ws(4096, 4096, 14336, 8, 2, moe.MOE_F32) > base
+    assert ws(0, 4096, 14336, 8, 2, moe.MOE_BF16) > 0       # T = 0 is legal
+    for bad in [(-1, 64, 64, 8, 2), (8, 100, 64, 8, 2), (8, 64, 96, 8, 2), (8, 64, 64, 65, 2),
+                (8, 64, 64, 8, 9), (8, 64, 64, 4, 5), (8, 64, 64, 8, 0), (1 << 30, 64, 64, 8, 2)]:
+        assert ws(*bad, moe.MOE_BF16) == 0, bad
+
+
+def _rc(name, *args):
+    return getattr(moe.lib(), name)(*args)
+
+
+def test_forward_argument_checks_return_codes():
+    f = "moe_forward"
+    ok_args = dict(x=FAKE, Wg=FAKE, W1=FAKE, W3=FAKE, W2=FAKE, dt=moe.MOE_BF16, T=32, d=128,
+                   d_ff=256, E=8, k=2, y=FAKE, ws=FAKE, ws_bytes=0, stream=None)
+
+    def call(**over):
+        a = dict(ok_args, **over)
+        return _rc(f, a["x"], a["Wg"], a["W1"], a["W3"], a["W2"], a["dt"], a["T"], a["d"],
+                   a["d_ff"], a["E"], a["k"], a["y"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert call(ws_bytes=0) == moe.MOE_ERR_WORKSPACE
+    assert "workspace" in moe.lib().moe_last_error().decode()
+    assert call(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(W2=ctypes.c_void_p((1 << 20) + 8)) == moe.MOE_ERR_INVALID_ARG  # misaligned
+    assert call(k=9) == moe.MOE_ERR_UNSUPPORTED
+    assert call(E=65) == moe.MOE_ERR_UNSUPPORTED
+    assert call(d=100) == moe.MOE_ERR_UNSUPPORTED
+    assert call(d_ff=200) == moe.MOE_ERR_UNSUPPORTED
+    assert call(T=-5) == moe.MOE_ERR_INVALID_ARG
+    assert call(dt=7) == moe.MOE_ERR_INVALID_ARG
+    # T = 0 enqueues nothing and succeeds even with NULL buffers
+    assert call(T=0, x=None, y=None, ws=None) == moe.MOE_OK
+
+
+def test_other_entry_points_reject_before_launch():
+    L = moe.lib()
+    assert L.moe_route(None, FAKE, moe.MOE_BF16, 4, 64, 8, 2, FAKE, FAKE, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(FAKE, FAKE, moe.MOE_BF16, 4, 64, 8, 0, FAKE, FAKE, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, moe.MOE_BF16, 4, 64, 64, 8, 2, FAKE,
+                            FAKE, 16, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, moe.MOE_BF16, 4, 64, 2, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_rmsnorm(FAKE, moe.MOE_BF16, 4, 64, ctypes.c_float(-1.0), FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_block_forward(FAKE, FAKE, FAKE, FAKE, FAKE, moe.MOE_BF16, 4, 64, 64, 8, 2,
+                               ctypes.c_float(1e-5), None, None, FAKE, 0, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert L.moe_permute(FAKE, FAKE, moe.MOE_BF16, 4, 64, 8, 2, None, FAKE, FAKE, FAKE, FAKE,
+                         None, 0, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        moe.lib()
