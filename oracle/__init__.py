@@ -45,14 +45,14 @@ def lib():
         L.orc_router_logits.argtypes = [P, i32, P, i64, i32, i32, P, i32]
         L.orc_topk_gates.argtypes = [P, i64, i32, i32, P, P, P, P]
         L.orc_permute.argtypes = [P, i64, i32, i32, P, P, P, P]
-        L.orc_swiglu_expert.argtypes = [P, P, P, P, i32, i32, i32, i32, P]
-        L.orc_moe_rows.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32, P, i64,
+        L.orc_swiglu_expert.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P]
+        L.orc_moe_rows.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, P, i64,
                                    P, P, P, P, P, i32]
         L.orc_rmsnorm.argtypes = [P, i32, dbl, P]
         L.orc_rmsnorm_rows.argtypes = [P, i64, i32, dbl, i32, P]
         L.orc_rmsnorm_rows.restype = ctypes.c_int
-        L.orc_block_step.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, dbl, P, P, P, P,
-                                     i32]
+        L.orc_block_step.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, dbl, i32, P, P, P,
+                                     P, i32]
         for name in ("orc_router_logits", "orc_topk_gates", "orc_permute", "orc_swiglu_expert",
                      "orc_moe_rows", "orc_rmsnorm", "orc_block_step"):
             getattr(L, name).restype = ctypes.c_int
@@ -146,8 +146,9 @@ def permute(idx, E):
     return dict(counts=counts, offsets=offsets, row_of=row_of, token_of=token_of)
 
 
-def swiglu_expert(xrow, W1, W3, W2, e):
-    """One expert on one fp64 row: W2_e (silu(W1_e x) * W3_e x)."""
+def swiglu_expert(xrow, W1, W3, W2, e, round_mid=False):
+    """One expert on one fp64 row: W2_e (silu(W1_e x) * W3_e x); round_mid
+    rounds the intermediate to bf16 before W2."""
     w1, dt = _raw(W1)
     w3, dt3 = _raw(W3)
     w2, dt2 = _raw(W2)
@@ -157,12 +158,13 @@ def swiglu_expert(xrow, W1, W3, W2, e):
     assert xr.shape == (d,)
     out = np.empty(d, np.float64)
     _check(lib().orc_swiglu_expert(_ptr(xr), _ptr(w1), _ptr(w3), _ptr(w2), dt, int(e), d, d_ff,
-                                   _ptr(out)), "swiglu_expert")
+                                   int(bool(round_mid)), _ptr(out)), "swiglu_expert")
     return out
 
 
-def moe_rows(x, Wg, W1, W3, W2, k, rows=None, nthreads=None):
-    """The whole layer for the listed rows of x (default: all rows).
+def moe_rows(x, Wg, W1, W3, W2, k, rows=None, nthreads=None, round_mid=False):
+    """The whole layer for the listed rows of x (default: all rows).  round_mid
+    rounds each expert's SwiGLU intermediate to bf16 before W2.
 
     Returns dict y f64[n][d], idx, gates, gap_order, gap_set.
     """
@@ -184,7 +186,8 @@ def moe_rows(x, Wg, W1, W3, W2, k, rows=None, nthreads=None):
     go = np.empty(n, np.float64)
     gs = np.empty(n, np.float64)
     _check(lib().orc_moe_rows(_ptr(xa), xdt, _ptr(wg), _ptr(w1), _ptr(w3), _ptr(w2), wdt, d,
-                              d_ff, E, k, _ptr(rows), n, _ptr(y), _ptr(idx), _ptr(gates),
+                              d_ff, E, k, int(bool(round_mid)), _ptr(rows), n, _ptr(y), _ptr(idx),
+                              _ptr(gates),
                               _ptr(go), _ptr(gs), nthreads or default_threads()), "moe_rows")
     return dict(y=y, idx=idx, gates=gates, gap_order=go, gap_set=gs)
 
@@ -206,8 +209,11 @@ def rmsnorm_rows(h, eps, round_bf16=True):
     return out
 
 
-def block_step(h, Wg, W1, W3, W2, k, eps, nthreads=None):
+def block_step(h, Wg, W1, W3, W2, k, eps, round_mid=False, nthreads=None):
     """One block h <- bf16(h + moe(bf16(rmsnorm(h)))) on n independent rows.
+
+    round_mid rounds each expert's SwiGLU intermediate to bf16 (the one
+    quantisation point a bf16 matrix-core data path adds inside the layer).
 
     h: f64[n][d] holding bf16 values; updated in place.  Weights bf16.
     Returns the step's routing dict (idx, gates, gap_order, gap_set).
@@ -225,7 +231,8 @@ def block_step(h, Wg, W1, W3, W2, k, eps, nthreads=None):
     go = np.empty(n, np.float64)
     gs = np.empty(n, np.float64)
     _check(lib().orc_block_step(_ptr(h), n, _ptr(wg), _ptr(w1), _ptr(w3), _ptr(w2), d, d_ff, E,
-                                k, float(eps), _ptr(idx), _ptr(gates), _ptr(go), _ptr(gs),
+                                k, float(eps), int(bool(round_mid)), _ptr(idx), _ptr(gates),
+                                _ptr(go), _ptr(gs),
                                 nthreads or default_threads()), "block_step")
     return dict(idx=idx, gates=gates, gap_order=go, gap_set=gs)
 

@@ -217,9 +217,11 @@ int orc_permute(const int32_t *idx, long T, int E, int k, int32_t *counts,
 static double silu(double u) { return u / (1.0 + exp(-u)); }
 
 /* E(x) = w2(silu(w1 x) * w3 x)  [tokentrails lineage, Code listing;
- * fdeinterviews breakdown: each expert is a SwiGLU block]. */
+ * fdeinterviews breakdown: each expert is a SwiGLU block].  With round_mid
+ * the intermediate silu(w1 x) * w3 x is rounded to bf16 before w2 (the
+ * quantisation point of a bf16 data path). */
 int orc_swiglu_expert(const double *x, const void *W1, const void *W3, const void *W2,
-                      int w_dt, int e, int d, int d_ff, double *out) {
+                      int w_dt, int e, int d, int d_ff, int round_mid, double *out) {
     if (!x || !W1 || !W3 || !W2 || !out || d < 1 || d_ff < 1 || e < 0) return -1;
     double *h = (double *)malloc(sizeof(double) * (size_t)d_ff);
     if (!h) return -1;
@@ -231,6 +233,7 @@ int orc_swiglu_expert(const double *x, const void *W1, const void *W3, const voi
             v += load_elem(W3, w_dt, base13 + (size_t)j * d + i) * x[i];
         }
         h[j] = silu(u) * v;
+        if (round_mid) h[j] = orc_bf16_round(h[j]);
     }
     size_t base2 = (size_t)e * d * d_ff;
     for (int i = 0; i < d; ++i) {
@@ -248,8 +251,9 @@ int orc_swiglu_expert(const double *x, const void *W1, const void *W3, const voi
  * never evaluated and its weights are never read [flashpapers summary, "How
  * It Works"; ennepo lecture: six experts' parameters are not touched]. */
 static int moe_one(const double *x, const float *Wg, const void *W1, const void *W3,
-                   const void *W2, int w_dt, int d, int d_ff, int E, int k, double *y,
-                   int32_t *idx, double *gates, double *gap_order, double *gap_set) {
+                   const void *W2, int w_dt, int d, int d_ff, int E, int k, int round_mid,
+                   double *y, int32_t *idx, double *gates, double *gap_order,
+                   double *gap_set) {
     double l[64];
     double g[64];
     int32_t sel[64];
@@ -263,7 +267,7 @@ static int moe_one(const double *x, const float *Wg, const void *W1, const void 
     if (!o) return -1;
     for (int i = 0; i < d; ++i) y[i] = 0.0;
     for (int j = 0; j < k; ++j) {
-        if (orc_swiglu_expert(x, W1, W3, W2, w_dt, sel[j], d, d_ff, o) != 0) {
+        if (orc_swiglu_expert(x, W1, W3, W2, w_dt, sel[j], d, d_ff, round_mid, o) != 0) {
             free(o);
             return -1;
         }
@@ -282,7 +286,7 @@ typedef struct {
     int x_dt;
     const float *Wg;
     const void *W1, *W3, *W2;
-    int w_dt, d, d_ff, E, k;
+    int w_dt, d, d_ff, E, k, round_mid;
     const int64_t *rows;
     double *y;
     int32_t *idx;
@@ -300,7 +304,7 @@ static void rows_range(void *p, long lo, long hi) {
     for (long n = lo; n < hi; ++n) {
         size_t r = (size_t)c->rows[n];
         for (int i = 0; i < c->d; ++i) xr[i] = load_elem(c->x, c->x_dt, r * c->d + i);
-        if (moe_one(xr, c->Wg, c->W1, c->W3, c->W2, c->w_dt, c->d, c->d_ff, c->E, c->k,
+        if (moe_one(xr, c->Wg, c->W1, c->W3, c->W2, c->w_dt, c->d, c->d_ff, c->E, c->k, c->round_mid,
                     c->y + (size_t)n * c->d, c->idx ? c->idx + (size_t)n * c->k : NULL,
                     c->gates ? c->gates + (size_t)n * c->k : NULL,
                     c->gap_order ? c->gap_order + n : NULL,
@@ -312,12 +316,12 @@ static void rows_range(void *p, long lo, long hi) {
 
 int orc_moe_rows(const void *x, int x_dt, const float *Wg, const void *W1,
                  const void *W3, const void *W2, int w_dt, int d, int d_ff, int E,
-                 int k, const int64_t *rows, long n, double *y, int32_t *idx,
+                 int k, int round_mid, const int64_t *rows, long n, double *y, int32_t *idx,
                  double *gates, double *gap_order, double *gap_set, int nthreads) {
     if (n < 0 || d < 1 || d_ff < 1 || E < 1 || E > 64 || k < 1 || k > E) return -1;
     if (n > 0 && (!x || !Wg || !W1 || !W3 || !W2 || !rows || !y)) return -1;
-    rows_ctx c = {x, x_dt, Wg, W1, W3, W2, w_dt, d, d_ff, E, k, rows, y, idx, gates,
-                  gap_order, gap_set, 0};
+    rows_ctx c = {x, x_dt, Wg, W1, W3, W2, w_dt, d, d_ff, E, k, round_mid, rows, y, idx,
+                  gates, gap_order, gap_set, 0};
     parallel_for(n, nthreads, rows_range, &c);
     return c.failed ? -1 : 0;
 }
@@ -349,7 +353,7 @@ typedef struct {
     double *h;
     const float *Wg;
     const void *W1, *W3, *W2;
-    int d, d_ff, E, k;
+    int d, d_ff, E, k, round_mid;
     double eps;
     int32_t *idx;
     double *gates, *gap_order, *gap_set;
@@ -370,7 +374,7 @@ static void block_range(void *p, long lo, long hi) {
         double *h = c->h + (size_t)n * c->d;
         orc_rmsnorm(h, c->d, c->eps, xn);
         for (int i = 0; i < c->d; ++i) xn[i] = orc_bf16_round(xn[i]); /* bf16 activations */
-        if (moe_one(xn, c->Wg, c->W1, c->W3, c->W2, 1, c->d, c->d_ff, c->E, c->k, y,
+        if (moe_one(xn, c->Wg, c->W1, c->W3, c->W2, 1, c->d, c->d_ff, c->E, c->k, c->round_mid, y,
                     c->idx ? c->idx + (size_t)n * c->k : NULL,
                     c->gates ? c->gates + (size_t)n * c->k : NULL,
                     c->gap_order ? c->gap_order + n : NULL,
@@ -383,12 +387,13 @@ static void block_range(void *p, long lo, long hi) {
 }
 
 int orc_block_step(double *h, long n, const float *Wg, const void *W1, const void *W3,
-                   const void *W2, int d, int d_ff, int E, int k, double eps,
+                   const void *W2, int d, int d_ff, int E, int k, double eps, int round_mid,
                    int32_t *idx, double *gates, double *gap_order, double *gap_set,
                    int nthreads) {
     if (n < 0 || d < 1 || d_ff < 1 || E < 1 || E > 64 || k < 1 || k > E) return -1;
     if (n > 0 && (!h || !Wg || !W1 || !W3 || !W2)) return -1;
-    block_ctx c = {h, Wg, W1, W3, W2, d, d_ff, E, k, eps, idx, gates, gap_order, gap_set, 0};
+    block_ctx c = {h,   Wg,   W1, W3,  W2,    d,         d_ff,    E, k,
+                   round_mid, eps, idx, gates, gap_order, gap_set, 0};
     parallel_for(n, nthreads, block_range, &c);
     return c.failed ? -1 : 0;
 }

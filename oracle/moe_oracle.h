@@ -60,16 +60,18 @@ int orc_topk_gates(const double *logits, long T, int E, int k, int32_t *idx,
 int orc_permute(const int32_t *idx, long T, int E, int k, int32_t *counts,
                 int32_t *offsets, int32_t *row_of, int32_t *token_of);
 
-/* One expert on one input row x[d] (fp64): out[d] = W2_e (silu(W1_e x) * W3_e x). */
+/* One expert on one input row x[d] (fp64): out[d] = W2_e (silu(W1_e x) * W3_e x).
+ * round_mid != 0 rounds the intermediate silu(W1_e x) * W3_e x to bf16 first. */
 int orc_swiglu_expert(const double *x, const void *W1, const void *W3, const void *W2,
-                      int w_dt, int e, int d, int d_ff, double *out);
+                      int w_dt, int e, int d, int d_ff, int round_mid, double *out);
 
 /* The whole layer for a list of rows (rows[n] indexes x).  Outputs per listed
  * row: y[n][d] (fp64), idx[n][k], gates[n][k], gap_order[n], gap_set[n]
- * (NULL to skip).  Threads split the list statically. */
+ * (NULL to skip).  round_mid as for orc_swiglu_expert.  Threads split the
+ * list statically. */
 int orc_moe_rows(const void *x, int x_dt, const float *Wg, const void *W1,
                  const void *W3, const void *W2, int w_dt, int d, int d_ff, int E,
-                 int k, const int64_t *rows, long n, double *y, int32_t *idx,
+                 int k, int round_mid, const int64_t *rows, long n, double *y, int32_t *idx,
                  double *gates, double *gap_order, double *gap_set, int nthreads);
 
 /* RMSNorm with unit gain: out_i = h_i / sqrt(mean(h^2) + eps), fp64. */
@@ -82,9 +84,10 @@ int orc_rmsnorm_rows(const double *h, long n, int d, double eps, int round_bf16,
 /* One decoder-block MoE step on n independent rows held as bf16 values in
  * fp64 (h[n][d], updated in place):
  *     xn = bf16(rmsnorm(h));  h <- bf16(h + moe(xn)).
- * Weights are bf16.  Routing of the step is returned as for orc_moe_rows. */
+ * Weights are bf16; round_mid as for orc_swiglu_expert.  Routing of the step
+ * is returned as for orc_moe_rows. */
 int orc_block_step(double *h, long n, const float *Wg, const void *W1, const void *W3,
-                   const void *W2, int d, int d_ff, int E, int k, double eps,
+                   const void *W2, int d, int d_ff, int E, int k, double eps, int round_mid,
                    int32_t *idx, double *gates, double *gap_order, double *gap_set,
                    int nthreads);
 

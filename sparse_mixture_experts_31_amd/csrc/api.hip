@@ -74,7 +74,7 @@ size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace segments of the fused calls, in order.
 struct Carve {
-    size_t idx, gw, counts, offsets, row_of, token_of, o_perm, h, xn, total;
+    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, total;
 };
 
 Carve carve(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt) {
@@ -87,7 +87,8 @@ Carve carve(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt) {
     c.offsets = o;  o += up((size_t)(E + 1) * 4);
     c.row_of = o;   o += up(A * 4);
     c.token_of = o; o += up(A * 4);
-    c.o_perm = o;   o += up(A * d * es);
+    c.x_perm = o;   o += up(A * d * es);
+    c.o_perm = o;   o += up(A * d * 4);  // expert outputs stay fp32 until combined
     c.h = o;        o += up(A * d_ff * es);
     c.xn = o;       o += up((size_t)T * d * es);
     c.total = o;
@@ -182,8 +183,8 @@ moe_status moe_expert_ffn(const void *x_perm, const int32_t *offsets, const void
     if (!ws || ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
     REQUIRE_PTR(ws, kAlign);
-    LAUNCH(moe_launch_expert_ffn(x_perm, nullptr, offsets, W1, W3, W2, (int)dt, T * k, d, d_ff,
-                                 E, ws, out_perm, nullptr, (hipStream_t)stream),
+    LAUNCH(moe_launch_expert_ffn(x_perm, offsets, W1, W3, W2, (int)dt, 0, T * k, d, d_ff, E, ws,
+                                 out_perm, nullptr, (hipStream_t)stream),
            "expert_ffn");
     return ok();
 }
@@ -199,7 +200,7 @@ moe_status moe_combine(const void *out_perm, const int32_t *row_of, const float 
     REQUIRE_PTR(y, 16);
     if (residual_or_null && !aligned(residual_or_null, 16))
         return fail(MOE_ERR_INVALID_ARG, "residual_or_null is not 16-byte aligned");
-    LAUNCH(moe_launch_combine(out_perm, row_of, topk_w, residual_or_null, (int)dt, T, d, k, y,
+    LAUNCH(moe_launch_combine(out_perm, 0, row_of, topk_w, residual_or_null, (int)dt, T, d, k, y,
                               (hipStream_t)stream),
            "combine");
     return ok();
@@ -216,6 +217,7 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
     int32_t *offsets = at<int32_t>(ws, c.offsets);
     int32_t *row_of = at<int32_t>(ws, c.row_of);
     int32_t *token_of = at<int32_t>(ws, c.token_of);
+    void *x_perm = at<char>(ws, c.x_perm);
     void *o_perm = at<char>(ws, c.o_perm);
     void *hbuf = at<char>(ws, c.h);
     const int64_t A = T * k;
@@ -227,14 +229,17 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
     LAUNCH(mark(1), "event");
     LAUNCH(moe_launch_dispatch_index(idx, A, E, k, counts, offsets, row_of, token_of, s),
            "dispatch");
+    // The expert GEMMs read contiguous rows: copy each token's row to its k
+    // places in expert order first.
+    LAUNCH(moe_launch_gather_rows(x, (int)dt, T, d, k, row_of, x_perm, s), "gather");
     LAUNCH(mark(2), "event");
-    // GEMM1 reads each expert's token rows straight from x through token_of,
-    // so the fused path never materialises x_perm.
-    LAUNCH(moe_launch_expert_ffn(x, token_of, offsets, W1, W3, W2, (int)dt, A, d, d_ff, E, hbuf,
+    // The W2 GEMM leaves the expert outputs in fp32; the combine rounds once.
+    LAUNCH(moe_launch_expert_ffn(x_perm, offsets, W1, W3, W2, (int)dt, 1, A, d, d_ff, E, hbuf,
                                  o_perm, ev ? (hipEvent_t)ev[3] : nullptr, s),
            "expert_ffn");
     LAUNCH(mark(4), "event");
-    LAUNCH(moe_launch_combine(o_perm, row_of, gw, residual, (int)dt, T, d, k, y, s), "combine");
+    LAUNCH(moe_launch_combine(o_perm, 1, row_of, gw, residual, (int)dt, T, d, k, y, s),
+           "combine");
     LAUNCH(mark(5), "event");
     return ok();
 }

@@ -50,9 +50,11 @@ struct Vec8<float> {
 
 constexpr int kRowWaves = 4;
 
-template <typename T>
+// TI: type of the expert outputs (the activation type, or fp32 when the
+// fused layer keeps them unrounded); T: residual and output type.
+template <typename TI, typename T>
 __global__ __launch_bounds__(kRowWaves *kWave) void combine_kernel(
-    const T *__restrict__ out_perm, const int32_t *__restrict__ row_of,
+    const TI *__restrict__ out_perm, const int32_t *__restrict__ row_of,
     const float *__restrict__ gw, const T *residual, int64_t T_, int d, int k, T *y) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t t = (int64_t)blockIdx.x * kRowWaves + threadIdx.x / kWave;
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kRowWaves *kWave) void combine_kernel(
         for (int j = 0; j < 8; ++j) {
             if (rows[j] >= 0) {
                 float o[8];
-                Vec8<T>::load(out_perm + (int64_t)rows[j] * d + i, o);
+                Vec8<TI>::load(out_perm + (int64_t)rows[j] * d + i, o);
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc[c] = fmaf(g[j], o[c], acc[c]);
             }
@@ -134,17 +136,23 @@ __global__ __launch_bounds__(kRowWaves *kWave) void rmsnorm_kernel(const T *h, i
 
 }  // namespace moe
 
-hipError_t moe_launch_combine(const void *out_perm, const int32_t *row_of, const float *gw,
-                              const void *residual, int dt, int64_t T, int d, int k, void *y,
-                              hipStream_t s) {
+hipError_t moe_launch_combine(const void *out_perm, int out_f32, const int32_t *row_of,
+                              const float *gw, const void *residual, int dt, int64_t T, int d,
+                              int k, void *y, hipStream_t s) {
     using namespace moe;
     const dim3 grid((unsigned)((T + kRowWaves - 1) / kRowWaves)), block(kRowWaves * kWave);
     if (dt == 0)
-        hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, (const float *)out_perm,
-                           row_of, gw, (const float *)residual, T, d, k, (float *)y);
+        hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s,
+                           (const float *)out_perm, row_of, gw, (const float *)residual, T, d, k,
+                           (float *)y);
+    else if (out_f32)
+        hipLaunchKernelGGL((combine_kernel<float, bf16_t>), grid, block, 0, s,
+                           (const float *)out_perm, row_of, gw, (const bf16_t *)residual, T, d, k,
+                           (bf16_t *)y);
     else
-        hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, s, (const bf16_t *)out_perm,
-                           row_of, gw, (const bf16_t *)residual, T, d, k, (bf16_t *)y);
+        hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), grid, block, 0, s,
+                           (const bf16_t *)out_perm, row_of, gw, (const bf16_t *)residual, T, d,
+                           k, (bf16_t *)y);
     return hipGetLastError();
 }
 

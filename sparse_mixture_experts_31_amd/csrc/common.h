@@ -66,16 +66,21 @@ hipError_t moe_launch_dispatch_index(const int32_t *idx, int64_t A, int E, int k
                                      int32_t *token_of, hipStream_t s);
 hipError_t moe_launch_gather_rows(const void *x, int dt, int64_t T, int d, int k,
                                   const int32_t *row_of, void *x_perm, hipStream_t s);
-// Grouped expert GEMMs.  `gather` (may be NULL) maps a row of an expert's
-// block to the activation row it reads (token_of); NULL means the activation
-// is already in expert order (x_perm).  `mid_event` (may be NULL) is recorded
-// between the W1/W3 GEMM and the W2 GEMM.
-hipError_t moe_launch_expert_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
-                                 const void *W1, const void *W3, const void *W2, int dt,
-                                 int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
+// Grouped expert GEMMs over activations already in expert order (x_perm).
+// `mid_event` (may be NULL) is recorded between the W1/W3 GEMM and the W2 GEMM.
+// `out_f32` != 0: the W2 GEMM writes fp32 expert outputs instead of dt.
+hipError_t moe_launch_expert_ffn(const void *act, const int32_t *offsets, const void *W1,
+                                 const void *W3, const void *W2, int dt, int out_f32, int64_t A,
+                                 int d, int d_ff, int E, void *hbuf, void *out,
                                  hipEvent_t mid_event, hipStream_t s);
-hipError_t moe_launch_combine(const void *out_perm, const int32_t *row_of, const float *gw,
-                              const void *residual, int dt, int64_t T, int d, int k, void *y,
-                              hipStream_t s);
+// The same experts for decode-sized batches (few rows per expert).
+hipError_t moe_launch_skinny_ffn(const void *x_perm, const int32_t *offsets, const void *W1,
+                                 const void *W3, const void *W2, int dt, int out_f32, int64_t A,
+                                 int d, int d_ff, int E, void *hbuf, void *out,
+                                 hipEvent_t mid_event, hipStream_t s);
+// `out_f32` != 0: out_perm holds fp32 expert outputs (y, residual stay dt).
+hipError_t moe_launch_combine(const void *out_perm, int out_f32, const int32_t *row_of,
+                              const float *gw, const void *residual, int dt, int64_t T, int d,
+                              int k, void *y, hipStream_t s);
 hipError_t moe_launch_rmsnorm(const void *h, int dt, int64_t T, int d, float eps, void *out,
                               hipStream_t s);

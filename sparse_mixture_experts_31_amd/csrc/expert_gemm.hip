@@ -8,29 +8,46 @@
 //   GEMM2 (SWIGLU=false): o[r][n] = sum_k h[r][k] W2_e[n][k]
 // Both operands are K-contiguous, the natural layout of the MFMA operands.
 //
-// Mapping.  A workgroup owns BN weight rows (n) of one expert — for GEMM1 the
-// same BN rows of both W1 and W3 — and BM token rows (m) of that expert.
-// Weights play the MFMA "A" operand (16 rows x 32 k) and tokens the "B"
-// operand (32 k x 16 cols) of v_mfma_f32_16x16x32_bf16 (fp32:
-// v_mfma_f32_16x16x4_f32, four per 16-byte fragment), accumulating in fp32.
-// An output fragment then holds four consecutive n of one token row, which
-// the epilogue writes as one 8-byte (bf16) or 16-byte (fp32) store.  The
-// silu(u) * v product is formed in registers from the u and v accumulators of
-// the same lane, so GEMM1 never writes u or v.
+// Tiles.  A tile is BW weight rows by BT token rows of one expert (for GEMM1
+// the BW rows are BW/2 rows of W1 and the same BW/2 rows of W3).  Weights
+// play the "A" operand and tokens the "B" operand of
+// v_mfma_f32_32x32x16_bf16 (fp32 data: four v_mfma_f32_32x32x2_f32 per
+// 16-byte fragment), accumulating in fp32.  On gfx950 the 32x32x16 form runs
+// at the full dense bf16 rate, twice the 16x16x32 form.  A lane of an output
+// fragment holds four runs of four consecutive n of one token row, each
+// written as one 8-byte (bf16) or 16-byte (fp32) store.  silu(u) * v is
+// formed in registers from the u and v accumulators of the same lane, so
+// GEMM1 never writes u or v.
 //
-// Pipeline.  K advances in stages of 128 bytes per row (64 bf16 / 32 fp32).
-// Each thread loads its share of the next stage with 16-byte global loads
-// into registers while the matrix cores work on the current stage from LDS;
-// the registers then go to the other LDS buffer (double buffering, one
-// barrier per stage).  LDS rows are 128 bytes with the 16-byte chunk index
-// XOR-swizzled by (row & 7), so the column of 16-byte reads an MFMA fragment
-// needs spreads across banks.
+// LDS layout.  K advances 64 bytes per stage (32 bf16 / 16 fp32).  A stage
+// holds BW + BT rows of 64 bytes; the four 16-byte chunks of row r sit at
+// chunk ^ ((r >> 2) & 3).  An MFMA operand read (32 rows, one chunk per
+// half-wave) then touches 16 distinct 16-byte bank groups in every group of
+// 16 lanes: no bank conflicts.
 //
-// Ragged tiles.  Token rows past the expert's count read a valid clamped row
-// and are never stored; weight rows past N are clamped likewise.  A
-// workgroup whose tile index lies beyond the experts' total tile count exits
-// at once (the grid is sized by an upper bound so the host never reads the
-// counts back).
+// Pipeline.  Rows move from global memory straight into LDS with
+// global_load_lds_dwordx4: one instruction moves 16 rows x 64 bytes, lane i
+// fetching the chunk that belongs at LDS offset 16 i.  No registers hold
+// tiles in flight.  A ring of P stages keeps P-1 stages in flight while one
+// is consumed: wait (vmcnt) for this wave's share of the stage, barrier,
+// issue the stage P-1 ahead into the slot every wave finished reading before
+// the barrier, then run the MFMAs.  The waits are explicit; the barrier
+// carries no memory fence (a fence would wait for every load in flight) but
+// compiler barriers keep the code order.
+//
+// Persistent tiles.  The grid is a fixed number of resident workgroups; each
+// walks a list of tiles, and the load ring runs across tile boundaries, so
+// the next tile's first stages are in flight while the current one finishes
+// and writes its output.  Workgroup b runs on XCD b % 8.  The tiles are cut
+// into eight contiguous ranges, one per XCD (token tiles fastest, then
+// weight tiles, then experts), and the workgroups of an XCD take consecutive
+// tiles of its range in lock step, so they share weight and token tiles in
+// that XCD's L2.
+//
+// Ragged tiles.  Token rows past the expert's count load a clamped valid row
+// and are never stored; 32-row fragments wholly past the count skip their
+// MFMAs.  Weight rows past N are clamped likewise.  The tile list is derived
+// on the device from the offsets, so the host never reads the counts back.
 #include "common.h"
 
 namespace moe {
@@ -46,22 +63,24 @@ struct ElemSize<bf16_t> {
     static constexpr int value = 2;
 };
 
-// acc += A_frag * B_frag over one 64-byte k-step: 16 rows x 16 cols.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// acc += A_frag * B_frag over one 32-byte k-step: 32 rows x 32 cols.
 template <typename T>
-__device__ __forceinline__ f32x4 mma_step(i32x4 a, i32x4 b, f32x4 c);
+__device__ __forceinline__ f32x16 mma_step(i32x4 a, i32x4 b, f32x16 c);
 
 template <>
-__device__ __forceinline__ f32x4 mma_step<bf16_t>(i32x4 a, i32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+__device__ __forceinline__ f32x16 mma_step<bf16_t>(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 template <>
-__device__ __forceinline__ f32x4 mma_step<float>(i32x4 a, i32x4 b, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a.x), __int_as_float(b.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a.y), __int_as_float(b.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a.z), __int_as_float(b.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a.w), __int_as_float(b.w), c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mma_step<float>(i32x4 a, i32x4 b, f32x16 c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.x), __int_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.y), __int_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.z), __int_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.w), __int_as_float(b.w), c, 0, 0, 0);
     return c;
 }
 
@@ -82,218 +101,328 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *out, float v0, float v1, 
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// s_waitcnt constraining vmcnt to N and lgkmcnt to 0 (expcnt free); gfx9
+// encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
 
-template <int BN, int BM, int WN, int WM, bool SWIGLU, typename T>
-struct GemmShape {
-    static constexpr int kThreads = WN * WM * kWave;
-    static constexpr int kWRows = SWIGLU ? 2 * BN : BN;  // weight rows staged per stage
-    static constexpr int kRows = kWRows + BM;
-    static constexpr int kStageBytes = kRows * 128;
-    static constexpr int kLdsBytes = 2 * kStageBytes;
-    static constexpr int kChunksPerThread = kRows * 8 / kThreads;
-    static constexpr int TN = BN / WN / 16;  // 16-row fragments per wave along n
-    static constexpr int TM = BM / WM / 16;  // 16-col fragments per wave along m
-    static constexpr int kKStep = 128 / ElemSize<T>::value;  // K elements per stage
-    static_assert(kRows * 8 % kThreads == 0, "stage must split evenly over threads");
-    static_assert(TN >= 1 && TM >= 1, "wave tile too small");
-    static_assert(BN % (WN * 16) == 0 && BM % (WM * 16) == 0, "tile shape");
+// Workgroup barrier without a memory fence: the explicit waits decide what
+// has landed in LDS; the empty asm statements and scheduling barriers keep
+// the compiler from moving memory operations across it.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const char *g, char *lds) {
+    __builtin_amdgcn_global_load_lds((const void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Byte offset of 16-byte chunk c of LDS row r within a stage.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+template <int BW, int BT, int WN, int WM, int P, bool SWIGLU, typename T>
+struct GemmCfg {
+    static constexpr int kWaves = WN * WM;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kRows = BW + BT;               // LDS rows per stage
+    static constexpr int LPW = kRows / 16 / kWaves;     // 16-row loads per wave per stage
+    static constexpr int kStageBytes = kRows * 64;
+    static constexpr int kLdsBytes = P * kStageBytes;
+    static constexpr int kCols = SWIGLU ? BW / 2 : BW;  // output columns per tile
+    static constexpr int WU = kCols / 32 / WN;          // 32-row weight fragments per wave (u)
+    static constexpr int WT = BT / 32 / WM;             // 32-row token fragments per wave
+    static constexpr int kKStep = 64 / ElemSize<T>::value;  // K elements per stage
+    static_assert(kRows % (16 * kWaves) == 0, "stage rows must split evenly over waves");
+    static_assert(WU >= 1 && WT >= 1, "wave tile too small");
+    static_assert(kCols % (32 * WN) == 0 && BT % (32 * WM) == 0, "tile shape");
+    static_assert(P >= 3, "ring needs at least three stages");
+    static_assert(LPW * (P - 2) < 64, "vmcnt range");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS capacity");
 };
 
-template <int BN, int BM, int WN, int WM, bool SWIGLU, typename T>
+struct TileInfo {
+    int e, row0, mrem, n0;
+};
+
+// T: activation and weight type; TO: output type (T, or fp32 for the expert
+// outputs the fused layer combines).
+template <int BW, int BT, int WN, int WM, int P, bool SWIGLU, typename T, typename TO>
 __global__ __launch_bounds__(WN *WM *kWave) void grouped_gemm_kernel(
-    const T *__restrict__ act, const int32_t *__restrict__ gather, int64_t act_ld,
-    const T *__restrict__ Wa, const T *__restrict__ Wb, const int32_t *__restrict__ offsets,
-    int E, int N, int K, int A, T *__restrict__ out, int n_tiles) {
-    using S = GemmShape<BN, BM, WN, WM, SWIGLU, T>;
-    constexpr int CPT = S::kChunksPerThread;
-    constexpr int TN = S::TN, TM = S::TM;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const T *__restrict__ act, int64_t act_ld, const T *__restrict__ Wa,
+    const T *__restrict__ Wb, const int32_t *__restrict__ offsets, int E, int N, int K, int A,
+    TO *__restrict__ out) {
+    using C = GemmCfg<BW, BT, WN, WM, P, SWIGLU, T>;
+    constexpr int WU = C::WU, WT = C::WT, LPW = C::LPW;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    // per expert: first row, row count, first tile number (tiles before it)
+    __shared__ int s_lo[64], s_cnt[64], s_first[65];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int bx = blockIdx.x % n_tiles;
-    const int by = blockIdx.x / n_tiles;
+    const int n_tiles = (N + C::kCols - 1) / C::kCols;
 
-    // Which expert and which of its token tiles this workgroup owns.  The
-    // offsets are clamped to [0, A] so that no row index leaves the buffers
+    // Offsets are clamped to [0, A] so that no row index leaves the buffers
     // even for a malformed offsets array.
-    int e = -1, mt = 0, before = 0, lo = 0, hi = 0;
-    for (int i = 0; i < E; ++i) {
-        lo = min(max(offsets[i], 0), A);
-        hi = min(max(offsets[i + 1], lo), A);
-        const int tiles = (hi - lo + BM - 1) / BM;
-        if (by < before + tiles) {
-            e = i;
-            mt = by - before;
-            break;
+    if (tid == 0) {
+        int first = 0;
+        for (int i = 0; i < E; ++i) {
+            const int lo = min(max(offsets[i], 0), A);
+            const int hi = min(max(offsets[i + 1], lo), A);
+            s_lo[i] = lo;
+            s_cnt[i] = hi - lo;
+            s_first[i] = first;
+            first += (hi - lo + BT - 1) / BT * n_tiles;
         }
-        before += tiles;
+        s_first[E] = first;
     }
-    if (e < 0) return;  // uniform over the workgroup
-    const int row0 = lo + mt * BM;
-    const int mrem = min(BM, hi - row0);
-    const int n0 = bx * BN;
-
-    // This thread's chunks of every stage: fixed rows, fixed 16-byte columns.
-    const char *src[CPT];
-    int dst[CPT];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int q = i * S::kThreads + tid;
-        const int r = q >> 3, c = q & 7;
-        dst[i] = swz(r, c);
-        if (r < S::kWRows) {
-            const T *W = (SWIGLU && r >= BN) ? Wb : Wa;
-            const int nr = min(n0 + (SWIGLU ? r % BN : r), N - 1);
-            src[i] = (const char *)(W + ((int64_t)e * N + nr) * K) + c * 16;
-        } else {
-            const int m = min(r - S::kWRows, mrem - 1);
-            const int64_t arow = gather ? (int64_t)gather[row0 + m] : (int64_t)(row0 + m);
-            src[i] = (const char *)(act + arow * act_ld) + c * 16;
-        }
-    }
-
-    f32x4 accu[TN][TM];
-    f32x4 accv[SWIGLU ? TN : 1][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            accu[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (SWIGLU) accv[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-
-    i32x4 regs[CPT];
-    const int n_stages = K / S::kKStep;
-    const int wn = wave % WN, wm = wave / WN;
-    const int wrow0 = wn * (BN / WN);  // this wave's first weight row (u block)
-    const int xrow0 = wm * (BM / WM);  // this wave's first token row
-
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) regs[i] = *(const i32x4 *)src[i];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) *(i32x4 *)(smem + dst[i]) = regs[i];
     __syncthreads();
+    const int total = s_first[E];
 
-    for (int s = 0; s < n_stages; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < n_stages) {
+    // This workgroup's tiles: XCD range, then round robin inside the XCD.
+    const int G8 = gridDim.x / 8;  // workgroups per XCD (grid is a multiple of 8)
+    const int xcd = blockIdx.x % 8, wj = blockIdx.x / 8;
+    const int range = (total + 7) / 8;
+    const int range_lo = xcd * range;
+    const int range_n = max(0, min(range, total - range_lo));
+    const int my_tiles = (range_n > wj) ? (range_n - wj + G8 - 1) / G8 : 0;
+    const int n_k = K / C::kKStep;  // stages per tile
+    const int n_stages = my_tiles * n_k;
+    if (n_stages == 0) return;  // uniform over the workgroup
+
+    auto tile_info = [&](int k) {
+        const int t = range_lo + wj + k * G8;
+        int i = 0;
+        while (i + 1 < E && s_first[i + 1] <= t) ++i;
+        const int rem = t - s_first[i];
+        const int mtiles = (s_cnt[i] + BT - 1) / BT;
+        TileInfo ti;
+        ti.e = i;
+        ti.row0 = s_lo[i] + (rem % mtiles) * BT;
+        ti.mrem = min(BT, s_lo[i] + s_cnt[i] - ti.row0);
+        ti.n0 = (rem / mtiles) * C::kCols;
+        return ti;
+    };
+
+    // Producer.  Row r of a stage is loaded by wave (r / 16) % waves, lane
+    // 4 (r % 16) + chunk slot; the lane fetches the chunk that belongs in that
+    // slot.  Inside the loop the only vector-memory instructions are these
+    // loads (and the output stores), so the explicit waits stay exact.
+    const char *src[LPW];
+    auto set_sources = [&](const TileInfo &ti) {
 #pragma unroll
-            for (int i = 0; i < CPT; ++i)
-                regs[i] = *(const i32x4 *)(src[i] + (int64_t)(s + 1) * 128);
-        }
-        const char *sW = smem + buf * S::kStageBytes;
-        const char *sX = sW + S::kWRows * 128;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int c = ks * 4 + (lane >> 4);
-            i32x4 xf[TM];
-#pragma unroll
-            for (int j = 0; j < TM; ++j) {
-                const int r = xrow0 + j * 16 + (lane & 15);
-                xf[j] = *(const i32x4 *)(sX + swz(r, c));
-            }
-#pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                const int r = wrow0 + i * 16 + (lane & 15);
-                const i32x4 wf = *(const i32x4 *)(sW + swz(r, c));
-#pragma unroll
-                for (int j = 0; j < TM; ++j) accu[i][j] = mma_step<T>(wf, xf[j], accu[i][j]);
+        for (int i = 0; i < LPW; ++i) {
+            const int r = (wave + C::kWaves * i) * 16 + (lane >> 2);  // LDS row
+            const int c = (lane & 3) ^ ((r >> 2) & 3);                // global chunk it holds
+            if (r < BW) {
+                const T *W = Wa;
+                int nr;
                 if constexpr (SWIGLU) {
-                    const i32x4 vf = *(const i32x4 *)(sW + swz(BN + r, c));
+                    W = (r < BW / 2) ? Wa : Wb;
+                    nr = ti.n0 + (r % (BW / 2));
+                } else {
+                    nr = ti.n0 + r;
+                }
+                nr = min(nr, N - 1);
+                src[i] = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + c * 16;
+            } else {
+                const int m = min(r - BW, ti.mrem - 1);
+                src[i] = (const char *)(act + (int64_t)(ti.row0 + m) * act_ld) + c * 16;
+            }
+        }
+    };
+    int p_k = 0, p_s = 0;  // producer cursor: tile, stage
+    auto issue_next = [&](int g) {
+        if (p_s == 0) set_sources(tile_info(p_k));
+        char *slot = smem + (g % P) * C::kStageBytes;
 #pragma unroll
-                    for (int j = 0; j < TM; ++j) accv[i][j] = mma_step<T>(vf, xf[j], accv[i][j]);
+        for (int i = 0; i < LPW; ++i)
+            dma16(src[i] + (int64_t)p_s * 64, slot + (wave + C::kWaves * i) * 1024);
+        if (++p_s == n_k) {
+            p_s = 0;
+            ++p_k;
+        }
+    };
+
+    f32x16 accu[WU][WT];
+    f32x16 accv[SWIGLU ? WU : 1][WT];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < WU; ++i)
+#pragma unroll
+            for (int j = 0; j < WT; ++j) {
+                accu[i][j] = f32x16{};
+                if constexpr (SWIGLU) accv[i][j] = f32x16{};
+            }
+    };
+    zero_acc();
+
+    const int wn = wave % WN, wm = wave / WN;
+    const int ur0 = wn * WU * 32;        // first u (or plain weight) row of this wave
+    const int tr0 = BW + wm * WT * 32;   // first token LDS row of this wave
+    const int lrow = lane & 31, lhalf = lane >> 5;
+
+    // MFMAs of one stage over the first `live` token fragments of the wave.
+    auto compute = [&](const char *slot, int live) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int c = 2 * t + lhalf;
+            i32x4 tf[WT];
+#pragma unroll
+            for (int j = 0; j < WT; ++j) tf[j] = *(const i32x4 *)(slot + lds_off(tr0 + j * 32 + lrow, c));
+#pragma unroll
+            for (int i = 0; i < WU; ++i) {
+                const int r = ur0 + i * 32 + lrow;
+                const i32x4 wf = *(const i32x4 *)(slot + lds_off(r, c));
+                i32x4 vf;
+                if constexpr (SWIGLU) vf = *(const i32x4 *)(slot + lds_off(BW / 2 + r, c));
+#pragma unroll
+                for (int j = 0; j < WT; ++j) {
+                    if (j < live) {
+                        accu[i][j] = mma_step<T>(wf, tf[j], accu[i][j]);
+                        if constexpr (SWIGLU) accv[i][j] = mma_step<T>(vf, tf[j], accv[i][j]);
+                    }
                 }
             }
         }
-        if (s + 1 < n_stages) {
-            char *nb = smem + (buf ^ 1) * S::kStageBytes;
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) *(i32x4 *)(nb + dst[i]) = regs[i];
-        }
-        __syncthreads();
-    }
+    };
 
-    // Epilogue: fragment (i, j) element q is D[n = 4*(lane/16) + q][m = lane % 16].
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-        const int n = n0 + wrow0 + i * 16 + 4 * (lane >> 4);
+    for (int g = 0; g < P - 1; ++g)
+        if (g < n_stages) issue_next(g);
+
+    TileInfo cur = tile_info(0);
+    // token fragments of this wave holding at least one real row (wave-uniform)
+    int live_t = __builtin_amdgcn_readfirstlane(min(WT, max(0, (cur.mrem - wm * WT * 32 + 31) / 32)));
+    int c_s = 0, c_k = 0;  // consumer cursor: stage within tile, tile
+    for (int g = 0; g < n_stages; ++g) {
+        if (g + P - 2 < n_stages)
+            wait_vmcnt_lgkm0<LPW * (P - 2)>();
+        else
+            wait_vmcnt_lgkm0<0>();
+        stage_barrier();
+        if (g + P - 1 < n_stages) issue_next(g + P - 1);
+
+        const char *slot = smem + (g % P) * C::kStageBytes;
+        compute(slot, live_t);
+
+        if (++c_s == n_k) {
+            // Epilogue of the tile: element q of fragment (i, j) is
+            // D[n = 8 (q / 4) + 4 lhalf + q % 4][m = lrow].
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-            const int m = xrow0 + j * 16 + (lane & 15);
-            if (m < mrem && n < N) {
-                float v[4];
+            for (int i = 0; i < WU; ++i) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    v[q] = accu[i][j][q];
-                    if constexpr (SWIGLU) v[q] = silu(v[q]) * accv[i][j][q];
+                for (int j = 0; j < WT; ++j) {
+                    const int m = wm * WT * 32 + j * 32 + lrow;
+                    if (m < cur.mrem) {
+                        TO *orow = out + (int64_t)(cur.row0 + m) * N;
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const int n = cur.n0 + ur0 + i * 32 + 8 * gq + 4 * lhalf;
+                            if (n < N) {
+                                float v[4];
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    v[q] = accu[i][j][4 * gq + q];
+                                    if constexpr (SWIGLU) v[q] = silu(v[q]) * accv[i][j][4 * gq + q];
+                                }
+                                store4<TO>(orow + n, v[0], v[1], v[2], v[3]);
+                            }
+                        }
+                    }
                 }
-                store4<T>(out + (int64_t)(row0 + m) * N + n, v[0], v[1], v[2], v[3]);
+            }
+            zero_acc();
+            c_s = 0;
+            if (++c_k < my_tiles) {
+                cur = tile_info(c_k);
+                live_t = __builtin_amdgcn_readfirstlane(
+                    min(WT, max(0, (cur.mrem - wm * WT * 32 + 31) / 32)));
             }
         }
     }
 }
 
-template <int BN, int BM, int WN, int WM, bool SWIGLU, typename T>
-static hipError_t launch_grouped(const void *act, const int32_t *gather, int64_t act_ld,
-                                 const void *Wa, const void *Wb, const int32_t *offsets, int E,
-                                 int N, int K, int64_t A, void *out, hipStream_t s) {
-    using S = GemmShape<BN, BM, WN, WM, SWIGLU, T>;
-    auto kern = grouped_gemm_kernel<BN, BM, WN, WM, SWIGLU, T>;
+static int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    return cus;
+}
+
+template <int BW, int BT, int WN, int WM, int P, bool SWIGLU, typename T, typename TO = T>
+static hipError_t launch_grouped(const void *act, int64_t act_ld, const void *Wa, const void *Wb,
+                                 const int32_t *offsets, int E, int N, int K, int64_t A,
+                                 void *out, int wg_per_cu, hipStream_t s) {
+    using C = GemmCfg<BW, BT, WN, WM, P, SWIGLU, T>;
+    auto kern = grouped_gemm_kernel<BW, BT, WN, WM, P, SWIGLU, T, TO>;
     // LDS beyond the 64 KiB default must be requested per kernel (the call
     // is cheap and keeps the library free of cached per-device state).
     hipError_t err = hipFuncSetAttribute((const void *)kern,
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         S::kLdsBytes);
+                                         C::kLdsBytes);
     if (err != hipSuccess) return err;
-    const int n_tiles = (N + BN - 1) / BN;
-    // sum_e ceil(c_e / BM) <= ceil(A / BM) + E - 1
-    const int64_t m_bound = (A + BM - 1) / BM + E - 1;
-    const int64_t blocks = (int64_t)n_tiles * m_bound;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(S::kThreads), S::kLdsBytes, s,
-                       (const T *)act, gather, act_ld, (const T *)Wa, (const T *)Wb, offsets,
-                       E, N, K, (int)A, (T *)out, n_tiles);
+    // Resident workgroups, a multiple of 8 (one share per XCD), and never
+    // more than the tile count can use: sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1.
+    const int64_t n_tiles = (N + C::kCols - 1) / C::kCols;
+    const int64_t tile_bound = n_tiles * ((A + BT - 1) / BT + E - 1);
+    int64_t grid = (int64_t)device_cus() * wg_per_cu;
+    grid = std::min<int64_t>(grid, (tile_bound + 7) / 8 * 8);
+    grid = std::max<int64_t>(8, grid / 8 * 8);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, s,
+                       (const T *)act, act_ld, (const T *)Wa, (const T *)Wb, offsets, E, N, K,
+                       (int)A, (TO *)out);
     return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_ffn_typed(const void *act, const int32_t *gather,
-                                   const int32_t *offsets, const void *W1, const void *W3,
-                                   const void *W2, int64_t A, int d, int d_ff, int E,
-                                   void *hbuf, void *out, hipEvent_t mid, hipStream_t s) {
+template <typename T, typename TO>
+static hipError_t launch_ffn_typed(const void *act, const int32_t *offsets, const void *W1,
+                                   const void *W3, const void *W2, int64_t A, int d, int d_ff,
+                                   int E, void *hbuf, void *out, hipEvent_t mid, hipStream_t s) {
     hipError_t err;
-    // Few rows per expert (decode): narrow token tiles so the weights stream
-    // once.  Many rows (prefill): wide tiles for operand reuse.
-    const bool few = A < 64LL * E;
-    if (few) {
-        err = launch_grouped<64, 32, 4, 1, true, T>(act, gather, d, W1, W3, offsets, E, d_ff, d,
-                                                     A, hbuf, s);
+    const int64_t per_expert = A / E;
+    if (per_expert <= 32)  // decode-sized: a weight stream, see skinny_gemm.hip
+        return moe_launch_skinny_ffn(act, offsets, W1, W3, W2, ElemSize<T>::value == 4 ? 0 : 1,
+                                     ElemSize<TO>::value == 4, A, d, d_ff, E, hbuf, out, mid, s);
+    if (per_expert <= 256) {
+        err = launch_grouped<128, 64, 2, 2, 6, true, T>(act, d, W1, W3, offsets, E, d_ff, d, A,
+                                                         hbuf, 2, s);
         if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
         if (err != hipSuccess) return err;
-        return launch_grouped<128, 32, 4, 1, false, T>(hbuf, nullptr, d_ff, W2, nullptr,
-                                                        offsets, E, d, d_ff, A, out, s);
+        return launch_grouped<128, 64, 2, 2, 6, false, T, TO>(hbuf, d_ff, W2, nullptr, offsets,
+                                                               E, d, d_ff, A, out, 2, s);
     }
-    err = launch_grouped<128, 128, 4, 2, true, T>(act, gather, d, W1, W3, offsets, E, d_ff, d,
-                                                   A, hbuf, s);
+    err = launch_grouped<256, 256, 4, 2, 4, true, T>(act, d, W1, W3, offsets, E, d_ff, d, A,
+                                                      hbuf, 1, s);
     if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
     if (err != hipSuccess) return err;
-    return launch_grouped<256, 128, 4, 2, false, T>(hbuf, nullptr, d_ff, W2, nullptr, offsets,
-                                                     E, d, d_ff, A, out, s);
+    return launch_grouped<256, 256, 4, 2, 4, false, T, TO>(hbuf, d_ff, W2, nullptr, offsets, E,
+                                                            d, d_ff, A, out, 1, s);
 }
 
 }  // namespace moe
 
-hipError_t moe_launch_expert_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
-                                 const void *W1, const void *W3, const void *W2, int dt,
-                                 int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
-                                 hipEvent_t mid, hipStream_t s) {
+hipError_t moe_launch_expert_ffn(const void *act, const int32_t *offsets, const void *W1,
+                                 const void *W3, const void *W2, int dt, int out_f32, int64_t A,
+                                 int d, int d_ff, int E, void *hbuf, void *out, hipEvent_t mid,
+                                 hipStream_t s) {
+    using moe::bf16_t;
     if (dt == 0)
-        return moe::launch_ffn_typed<float>(act, gather, offsets, W1, W3, W2, A, d, d_ff, E,
-                                            hbuf, out, mid, s);
-    return moe::launch_ffn_typed<moe::bf16_t>(act, gather, offsets, W1, W3, W2, A, d, d_ff, E,
-                                              hbuf, out, mid, s);
+        return moe::launch_ffn_typed<float, float>(act, offsets, W1, W3, W2, A, d, d_ff, E, hbuf,
+                                                   out, mid, s);
+    if (out_f32)
+        return moe::launch_ffn_typed<bf16_t, float>(act, offsets, W1, W3, W2, A, d, d_ff, E,
+                                                    hbuf, out, mid, s);
+    return moe::launch_ffn_typed<bf16_t, bf16_t>(act, offsets, W1, W3, W2, A, d, d_ff, E, hbuf,
+                                                 out, mid, s);
 }

@@ -6,8 +6,8 @@
 // TopK keeps the k best scores and the softmax runs over them alone
 // (flashpapers summary, "How It Works").
 //
-// One wavefront owns TPW tokens and treats the experts EG at a time.  Each
-// lane walks its strided share of d, 8 elements per step, and accumulates x_i * Wg_e,i in fp64: a bf16 or fp32
+// WPT wavefronts own TPW tokens and treat the experts EG at a time.  Each
+// lane walks its strided share of the wave's slice of d, 8 elements per step, and accumulates x_i * Wg_e,i in fp64: a bf16 or fp32
 // element times an fp32 weight is exact in fp64, so only the fp64 additions
 // round and the final fp32 score is (almost always) the correctly rounded
 // value of the exact dot product.  That keeps the discrete top-k choice
@@ -65,20 +65,28 @@ __device__ __forceinline__ void wave_reduce_halving(double (&v)[NV], int lane) {
 
 constexpr int kRouterWaves = 4;
 
-template <typename Tin, int TPW, int EG>
+// WPT waves share each group of TPW tokens, every wave covering a contiguous
+// 1/WPT of d; their fp64 partial sums meet in LDS and are added in wave order.
+template <typename Tin, int TPW, int EG, int WPT>
 __global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
     const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,
     int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits) {
-    __shared__ float s_logit[kRouterWaves][TPW][64];
+    constexpr int kGroups = kRouterWaves / WPT;  // token groups per workgroup
+    __shared__ float s_logit[kGroups][TPW][64];
+    __shared__ double s_part[kGroups][WPT][TPW * EG];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int64_t tok0 = ((int64_t)blockIdx.x * kRouterWaves + wave) * TPW;
+    const int grp = wave / WPT, part = wave % WPT;
+    const int64_t tok0 = ((int64_t)blockIdx.x * kGroups + grp) * TPW;
+    const int dpart = d / WPT;
+    const int dlo = part * dpart, dhi = dlo + dpart;
+    constexpr int lanes_per_value = 64 / (TPW * EG);
 
     for (int e0 = 0; e0 < E; e0 += EG) {
         double acc[TPW * EG];
 #pragma unroll
         for (int i = 0; i < TPW * EG; ++i) acc[i] = 0.0;
-        for (int i = lane * 8; i < d; i += kWave * 8) {
+        for (int i = dlo + lane * 8; i < dhi; i += kWave * 8) {
             float xv[TPW][8];
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
@@ -103,25 +111,29 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
             }
         }
         wave_reduce_halving<TPW * EG>(acc, lane);
-        constexpr int lanes_per_value = 64 / (TPW * EG);
-        if ((lane % lanes_per_value) == 0) {
-            const int vi = lane / lanes_per_value;
-            const int t = vi / EG, j = vi % EG;
-            if (e0 + j < E) s_logit[wave][t][e0 + j] = (float)acc[0];
+        if ((lane % lanes_per_value) == 0) s_part[grp][part][lane / lanes_per_value] = acc[0];
+        __syncthreads();
+        if (part == 0 && lane < TPW * EG) {
+            double v = s_part[grp][0][lane];
+#pragma unroll
+            for (int p2 = 1; p2 < WPT; ++p2) v += s_part[grp][p2][lane];
+            const int t = lane / EG, j = lane % EG;
+            if (e0 + j < E) s_logit[grp][t][e0 + j] = (float)v;
         }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // scores out (optional), coalesced over the wave's TPW x E block
+    if (part != 0) return;
+    // scores out (optional), coalesced over the group's TPW x E block
     if (out_logits) {
         for (int q = lane; q < TPW * E; q += kWave) {
             const int t = q / E, e = q % E;
-            if (tok0 + t < T) out_logits[(tok0 + t) * E + e] = s_logit[wave][t][e];
+            if (tok0 + t < T) out_logits[(tok0 + t) * E + e] = s_logit[grp][t][e];
         }
     }
     if (lane < TPW && tok0 + lane < T) {
         const int t = lane;
-        const float *L = s_logit[wave][t];
+        const float *L = s_logit[grp][t];
         uint64_t used = 0;
         int sel[8];
         float sl[8];
@@ -165,25 +177,25 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
 hipError_t moe_launch_router(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
                              int k, int32_t *idx, float *gw, float *logits, hipStream_t s) {
     using namespace moe;
-    // Few tokens: one token per wave spreads the row reads over more waves.
-    // Many tokens: four per wave so each gate-weight load serves four rows.
-    const int tpw = (T <= 2048) ? 1 : 4;
-    const int64_t per_block = (int64_t)kRouterWaves * tpw;
-    const dim3 grid((unsigned)((T + per_block - 1) / per_block));
     const dim3 block(kRouterWaves * kWave);
-    if (dt == 0) {
-        if (tpw == 1)
-            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8>), grid, block, 0, s,
+    // Few tokens: four waves split each token's row, so a small batch still
+    // spreads over many waves.  Many tokens: one wave holds four tokens, so
+    // each gate-weight load serves four rows.
+    if (T <= 2048) {
+        const dim3 grid((unsigned)T);
+        if (dt == 0)
+            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 4>), grid, block, 0, s,
                                (const float *)x, Wg, T, d, E, k, idx, gw, logits);
         else
-            hipLaunchKernelGGL((router_topk_kernel<float, 4, 4>), grid, block, 0, s,
-                               (const float *)x, Wg, T, d, E, k, idx, gw, logits);
-    } else {
-        if (tpw == 1)
-            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8>), grid, block, 0, s,
+            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 4>), grid, block, 0, s,
                                (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits);
+    } else {
+        const dim3 grid((unsigned)((T + 15) / 16));
+        if (dt == 0)
+            hipLaunchKernelGGL((router_topk_kernel<float, 4, 4, 1>), grid, block, 0, s,
+                               (const float *)x, Wg, T, d, E, k, idx, gw, logits);
         else
-            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 4, 4>), grid, block, 0, s,
+            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 4, 4, 1>), grid, block, 0, s,
                                (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits);
     }
     return hipGetLastError();

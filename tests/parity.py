@@ -57,3 +57,27 @@ def to_np(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         t = t.float()
     return t.numpy()
+
+
+def bf16_rne(a):
+    """Nearest bf16 values (ties to even) of float64 data, as float64."""
+    a = np.asarray(a, np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def bf16_step(a):
+    """Spacing of bf16 values at magnitude |a| (normal range)."""
+    _, e = np.frexp(np.asarray(a, np.float64))
+    return np.ldexp(1.0, e - 8)
+
+
+def check_near_rounding_floor(got, want_exact, slack=1.25):
+    """got (bf16 values) against the exact result: the normwise error may
+    exceed that of rounding the exact result to bf16 once only by `slack`.
+    Returns (error, floor)."""
+    got = np.asarray(got, np.float64)
+    floor = normwise(bf16_rne(want_exact), want_exact)
+    err = normwise(got, want_exact)
+    assert err <= slack * floor, (err, floor)
+    return err, floor

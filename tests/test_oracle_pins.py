@@ -199,6 +199,34 @@ def test_swiglu_wiring_closed_form():
     np.testing.assert_allclose(out, [3.0 * silu2 * -1.0, 0.0, silu1 * 2.0], rtol=1e-15)
 
 
+def test_swiglu_intermediate_rounding_closed_form():
+    """round_mid rounds silu(w1 x) * w3 x to bf16 before w2: with identity
+    weights the output is that rounded value itself.
+    silu(1) * 1 = 0.7310585786300049 -> 187/256 = 0.73046875;
+    silu(2) * 2 = 3.5231883119115298 -> 225/64 = 3.515625."""
+    eye = np.eye(2, dtype=np.float32)[None]
+    x = np.array([1.0, 2.0])
+    out = oracle.swiglu_expert(x, eye, eye, eye, 0, round_mid=True)
+    np.testing.assert_array_equal(out, [187 / 256, 225 / 64])
+    out = oracle.swiglu_expert(x, eye, eye, eye, 0)
+    np.testing.assert_allclose(out, [0.7310585786300049, 3.5231883119115298], rtol=1e-15)
+
+
+def test_block_step_intermediate_rounding_is_a_small_perturbation():
+    w = TINY.with_(dtype="bf16")
+    L = make_layer(w, "cpu", 14)
+    h1 = L["x"].double().numpy().copy()
+    h2 = h1.copy()
+    r1 = oracle.block_step(h1, L["Wg"], L["W1"], L["W3"], L["W2"], 2, 1e-5)
+    r2 = oracle.block_step(h2, L["Wg"], L["W1"], L["W3"], L["W2"], 2, 1e-5, round_mid=True)
+    np.testing.assert_array_equal(r1["idx"], r2["idx"])
+    d = np.abs(h1 - h2)
+    assert d.max() > 0                       # the rounding does act
+    # a relative change of at most 2^-9 in the intermediate, plus at most one
+    # bf16 step where the residual sum then rounds the other way
+    assert np.linalg.norm(h1 - h2) <= 2.0 ** -8 * np.linalg.norm(h1)
+
+
 def test_identical_experts_reduce_to_one_dense_swiglu():
     """With every expert equal the gates sum to one, so y is the dense SwiGLU
     of x whatever the routing."""
