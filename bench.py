@@ -85,23 +85,57 @@ def layer_work(w, n_active):
     return nbytes, flops
 
 
-def cpu_baseline(w, L, budget_tokens):
-    """The oracle, as it stands, on a bounded token sample of the same layer."""
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE scaled by a plain
+    copy of known size), or None when there is none or the kernel source has
+    changed since the counters were taken."""
+    import glob
+    import hashlib
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("bench-traffic "):
+                    continue
+                rec = json.loads(line[len("bench-traffic "):])
+                if rec.get("workload") != workload:
+                    continue
+                src = os.path.join(ROOT, rec["source"])
+                if not os.path.exists(src):
+                    return None
+                with open(src, "rb") as s:
+                    if hashlib.sha1(s.read()).hexdigest() != rec["source_sha1"]:
+                        return None
+                return int(rec["traffic_bytes"])
+    return None
+
+
+def cpu_baseline(w, L, budget_tokens, budget_s=10.0):
+    """The oracle, as it stands, on a bounded token sample of the same layer:
+    chunks of `budget_tokens` consecutive tokens until about `budget_s`
+    seconds of wall time have passed (tokens are independent, so tokens per
+    second over the sample is the layer's rate)."""
     import numpy as np
 
     import oracle
 
-    rows = np.arange(min(w.T, budget_tokens), dtype=np.int64)
     host = {n: L[n].cpu() for n in ("x", "Wg", "W1", "W3", "W2")}
     threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    oracle.moe_rows(host["x"], host["Wg"], host["W1"], host["W3"], host["W2"], w.k, rows=rows,
-                    nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": threads,
+    chunk = min(w.T, budget_tokens)
+    done, start, elapsed = 0, 0, 0.0
+    while elapsed < budget_s and done < 64 * w.T:
+        rows = (np.arange(chunk, dtype=np.int64) + start) % w.T
+        t0 = time.perf_counter()
+        oracle.moe_rows(host["x"], host["Wg"], host["W1"], host["W3"], host["W2"], w.k,
+                        rows=rows, nthreads=threads)
+        elapsed += time.perf_counter() - t0
+        done += chunk
+        start = (start + chunk) % w.T
+    return {"value": round(done / elapsed, 3), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"first {len(rows)} of the {w.T} tokens of the {w.name} workload "
-                      f"(tokens are independent), {dt:.1f} s wall on {threads} threads"}
+            "sample": f"{done} tokens of the {w.name} workload (T={w.T}) in chunks of {chunk}, "
+                      f"{elapsed:.1f} s wall on {threads} threads"}
 
 
 def main():
@@ -115,6 +149,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="oracle sample size (default sized to ~10-30 s)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times (a plain copy of known "
+                         "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -132,6 +169,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     w = WORKLOADS[args.workload]
     print(f"[bench] workload {w.name}: T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} k={w.k} "
           f"{w.dtype} blocks={w.blocks}", file=sys.stderr, flush=True)
@@ -189,7 +235,7 @@ def main():
     roofline = None
     if blocks is None:
         gemm1_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
-        if w.T * w.k < 64 * w.E:       # weight streaming: HBM-bound
+        if (w.T * w.k) // w.E <= 32:   # weight streaming (the skinny kernels): HBM-bound
             achieved = g_bytes / (gemm1_ms * 1e-3) / 1e9
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -199,7 +245,10 @@ def main():
             achieved = g_flops / (gemm1_ms * 1e-3) / 1e12
             roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
-        roofline["kernel"] = "grouped_gemm_kernel<SWIGLU> (W1/W3 + silu*v)"
+        roofline["traffic"] = measured_traffic(w.name)
+        roofline["kernel"] = ("skinny_gemm_kernel<SWIGLU> (W1/W3 + silu*v)"
+                              if (w.T * w.k) // w.E <= 32 else
+                              "grouped_gemm_kernel<SWIGLU> (W1/W3 + silu*v)")
         roofline["kernel_ms"] = round(gemm1_ms, 4)
         roofline["alg_bytes"] = g_bytes
         roofline["alg_flops"] = g_flops

@@ -80,7 +80,7 @@ size_t moe_workspace_size(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt
  *   -> topk_w fp32 [T][k]: softmax over the k kept scores (sums to 1)
  *   -> logits_or_null fp32 [T][E]: the scores (optional)
  * Defined by: ennepo lecture (router passage: a linear layer gives one score
- * per expert, a top-two mask sends the rest to -inf, a softmax leaves two
+ * per expert, all but the k best go to -inf, and a softmax leaves k
  * probabilities summing to one); flashpapers summary "How It Works". */
 moe_status moe_route(const void *x, const float *Wg, moe_dtype dt, int64_t T, int d, int E,
                      int k, int32_t *topk_idx, float *topk_w, float *logits_or_null,
@@ -109,7 +109,8 @@ moe_status moe_permute(const void *x, const int32_t *topk_idx, moe_dtype dt, int
  * x_perm, out_perm [T*k][d] (dt); offsets int32 [E+1] on the device (as
  * produced by moe_permute; offsets[E] <= T*k).  Rows at or beyond offsets[E]
  * are left untouched.  The SwiGLU intermediate (rows x d_ff) lives in ws.
- * Defined by: fdeinterviews breakdown ("each expert is a SwiGLU block");
+ * Defined by: fdeinterviews breakdown, "The paper in one minute" (the experts
+ * are SwiGLU blocks);
  * tokentrails lineage, Code listing (w2(silu(w1(x)) * w3(x))). */
 moe_status moe_expert_ffn(const void *x_perm, const int32_t *offsets, const void *W1,
                           const void *W3, const void *W2, moe_dtype dt, int64_t T, int d,

@@ -249,7 +249,8 @@ int orc_swiglu_expert(const double *x, const void *W1, const void *W3, const voi
 
 /* y = sum over the kept experts of g_i E_i(x); an expert whose gate is zero is
  * never evaluated and its weights are never read [flashpapers summary, "How
- * It Works"; ennepo lecture: six experts' parameters are not touched]. */
+ * It Works"; ennepo lecture, combine passage: the unchosen experts' weights
+ * stay unread]. */
 static int moe_one(const double *x, const float *Wg, const void *W1, const void *W3,
                    const void *W2, int w_dt, int d, int d_ff, int E, int k, int round_mid,
                    double *y, int32_t *idx, double *gates, double *gap_order,

@@ -115,7 +115,7 @@ def test_three_gate_formulations_agree():
         np.testing.assert_allclose(gates, ga, rtol=0, atol=1e-15)
         np.testing.assert_allclose(gates, gb, rtol=0, atol=1e-15)
         np.testing.assert_array_equal(idx, pi.numpy())
-        # the kept gates sum to one [ennepo lecture: two probabilities that sum to one]
+        # the kept gates add up to one [ennepo lecture, router passage]
         assert np.abs(gates.sum(1) - 1.0).max() <= 4 * np.finfo(np.float64).eps
 
 
@@ -256,7 +256,7 @@ def test_layer_equals_dense_gated_sum_over_all_experts():
 
 def test_unselected_experts_are_never_read():
     """NaN in every expert a token does not pick leaves its y bit-identical
-    (the six other experts' parameters are not touched)."""
+    (the unchosen experts' weights are never read; ennepo lecture, combine passage)."""
     w, L = _tiny(seed=6)
     r = oracle.moe_rows(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], 2)
     for t in (0, 13, 63):
