@@ -246,9 +246,14 @@ def main():
             roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
         roofline["traffic"] = measured_traffic(w.name)
-        roofline["kernel"] = ("skinny_gemm_kernel<SWIGLU> (W1/W3 + silu*v)"
-                              if (w.T * w.k) // w.E <= 32 else
-                              "grouped_gemm_kernel<SWIGLU> (W1/W3 + silu*v)")
+        per_expert = (w.T * w.k) // w.E
+        if per_expert <= 32:
+            kname = "skinny_gemm_kernel<SWIGLU>"
+        elif per_expert <= 256 or w.dtype == "f32":
+            kname = "grouped_gemm_kernel<SWIGLU>"
+        else:
+            kname = "wide_gemm_kernel<SWIGLU>"
+        roofline["kernel"] = kname + " (W1/W3 + silu*v)"
         roofline["kernel_ms"] = round(gemm1_ms, 4)
         roofline["alg_bytes"] = g_bytes
         roofline["alg_flops"] = g_flops

@@ -54,6 +54,9 @@ SMALL = [
     Workload("k1", 15, T=128, d=256, d_ff=512, k=1),
     Workload("one-token", 16, T=1, d=512, d_ff=512),
     Workload("wide-few", 17, T=700, d=320, d_ff=704, E=4, k=2),
+    # more wide tiles than workgroups (the load ring crosses tiles), the
+    # shortest k-loop (d = 128) and a W2 tile half past N
+    Workload("wide-many", 18, T=2048, d=128, d_ff=2304),
 ]
 
 
