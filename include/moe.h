@@ -108,7 +108,10 @@ moe_status moe_permute(const void *x, const int32_t *topk_idx, moe_dtype dt, int
  *     out_perm[r] = W2_e (silu(W1_e x_perm[r]) * W3_e x_perm[r])
  * x_perm, out_perm [T*k][d] (dt); offsets int32 [E+1] on the device (as
  * produced by moe_permute; offsets[E] <= T*k).  Rows at or beyond offsets[E]
- * are left untouched.  The SwiGLU intermediate (rows x d_ff) lives in ws.
+ * are left untouched.  ws holds the SwiGLU intermediate (rows x d_ff) and,
+ * for large bf16 batches, fp32 partial sums of tiles split along K (summed
+ * in a fixed order: results are deterministic); moe_workspace_size() bytes
+ * always suffice.
  * Defined by: fdeinterviews breakdown, "The paper in one minute" (the experts
  * are SwiGLU blocks);
  * tokentrails lineage, Code listing (w2(silu(w1(x)) * w3(x))). */

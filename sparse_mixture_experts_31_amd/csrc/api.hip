@@ -74,7 +74,8 @@ size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace segments of the fused calls, in order.
 struct Carve {
-    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, total;
+    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, split, total;
+    size_t split_bytes;
 };
 
 Carve carve(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt) {
@@ -91,6 +92,8 @@ Carve carve(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt) {
     c.o_perm = o;   o += up(A * d * 4);  // expert outputs stay fp32 until combined
     c.h = o;        o += up(A * d_ff * es);
     c.xn = o;       o += up((size_t)T * d * es);
+    c.split_bytes = moe_expert_ffn_scratch_bytes((int)dt, (int64_t)A, d, d_ff, E);
+    c.split = o;    o += up(c.split_bytes);  // partial sums of K-split expert tiles
     c.total = o;
     return c;
 }
@@ -179,12 +182,16 @@ moe_status moe_expert_ffn(const void *x_perm, const int32_t *offsets, const void
     REQUIRE_PTR(W3, 16);
     REQUIRE_PTR(W2, 16);
     REQUIRE_PTR(out_perm, 16);
-    const size_t need = up((size_t)T * k * d_ff * elem_size(dt));
+    // workspace: the SwiGLU intermediate, then scratch for K-split tiles
+    const size_t h_bytes = up((size_t)T * k * d_ff * elem_size(dt));
+    const size_t split_bytes = moe_expert_ffn_scratch_bytes((int)dt, T * k, d, d_ff, E);
+    const size_t need = h_bytes + split_bytes;
     if (!ws || ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
     REQUIRE_PTR(ws, kAlign);
     LAUNCH(moe_launch_expert_ffn(x_perm, offsets, W1, W3, W2, (int)dt, 0, T * k, d, d_ff, E, ws,
-                                 out_perm, nullptr, (hipStream_t)stream),
+                                 out_perm, split_bytes ? at<char>(ws, h_bytes) : nullptr,
+                                 split_bytes, nullptr, (hipStream_t)stream),
            "expert_ffn");
     return ok();
 }
@@ -235,7 +242,8 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
     LAUNCH(mark(2), "event");
     // The W2 GEMM leaves the expert outputs in fp32; the combine rounds once.
     LAUNCH(moe_launch_expert_ffn(x_perm, offsets, W1, W3, W2, (int)dt, 1, A, d, d_ff, E, hbuf,
-                                 o_perm, ev ? (hipEvent_t)ev[3] : nullptr, s),
+                                 o_perm, c.split_bytes ? at<char>(ws, c.split) : nullptr,
+                                 c.split_bytes, ev ? (hipEvent_t)ev[3] : nullptr, s),
            "expert_ffn");
     LAUNCH(mark(4), "event");
     LAUNCH(moe_launch_combine(o_perm, 1, row_of, gw, residual, (int)dt, T, d, k, y, s),

@@ -48,85 +48,9 @@
 // and are never stored; 32-row fragments wholly past the count skip their
 // MFMAs.  Weight rows past N are clamped likewise.  The tile list is derived
 // on the device from the offsets, so the host never reads the counts back.
-#include "common.h"
+#include "gemm_common.h"
 
 namespace moe {
-
-template <typename T>
-struct ElemSize;
-template <>
-struct ElemSize<float> {
-    static constexpr int value = 4;
-};
-template <>
-struct ElemSize<bf16_t> {
-    static constexpr int value = 2;
-};
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// acc += A_frag * B_frag over one 32-byte k-step: 32 rows x 32 cols.
-template <typename T>
-__device__ __forceinline__ f32x16 mma_step(i32x4 a, i32x4 b, f32x16 c);
-
-template <>
-__device__ __forceinline__ f32x16 mma_step<bf16_t>(i32x4 a, i32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ f32x16 mma_step<float>(i32x4 a, i32x4 b, f32x16 c) {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.x), __int_as_float(b.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.y), __int_as_float(b.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.z), __int_as_float(b.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.w), __int_as_float(b.w), c, 0, 0, 0);
-    return c;
-}
-
-template <typename T>
-__device__ __forceinline__ void store4(T *out, float v0, float v1, float v2, float v3);
-
-template <>
-__device__ __forceinline__ void store4<float>(float *out, float v0, float v1, float v2,
-                                              float v3) {
-    *(float4 *)out = make_float4(v0, v1, v2, v3);
-}
-
-template <>
-__device__ __forceinline__ void store4<bf16_t>(bf16_t *out, float v0, float v1, float v2,
-                                               float v3) {
-    *(uint2 *)out = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-}
-
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
-
-// s_waitcnt constraining vmcnt to N and lgkmcnt to 0 (expcnt free); gfx9
-// encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8].
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-// Workgroup barrier without a memory fence: the explicit waits decide what
-// has landed in LDS; the empty asm statements and scheduling barriers keep
-// the compiler from moving memory operations across it.
-__device__ __forceinline__ void stage_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void dma16(const char *g, char *lds) {
-    __builtin_amdgcn_global_load_lds((const void *)g,
-                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-
-// Byte offset of 16-byte chunk c of LDS row r within a stage.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
 template <int BW, int BT, int WN, int WM, int P, bool SWIGLU, typename T>
 struct GemmCfg {
@@ -148,9 +72,6 @@ struct GemmCfg {
     static_assert(kLdsBytes <= 160 * 1024, "LDS capacity");
 };
 
-struct TileInfo {
-    int e, row0, mrem, n0;
-};
 
 // T: activation and weight type; TO: output type (T, or fp32 for the expert
 // outputs the fused layer combines).
@@ -351,262 +272,6 @@ __global__ __launch_bounds__(WN *WM *kWave) void grouped_gemm_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
-// Wide tiles for bf16 prefill: 256 weight rows x 256 token rows per tile and
-// four waves in a 2 x 2 grid, each wave owning 128 x 128 outputs in 256
-// accumulator registers (one wave per SIMD).  Per 16-wide k-step a wave reads
-// four weight and four token fragments and issues 16 MFMAs: half the LDS
-// reads per MFMA of the 8-wave grouped_gemm_kernel, whose 64 x 128 wave tiles
-// keep the LDS read port as busy as the matrix cores.
-//
-// Same LDS stage layout, DMA ring and persistent XCD-ordered tile walk as
-// grouped_gemm_kernel, with three differences that keep the one wave per SIMD
-// issuing MFMAs:
-//  * Fragment double buffering: the second k-half of a stage is read while
-//    the MFMAs of the first half run, the next stage's first half while the
-//    second half's run; the reads and loads are interleaved one by one with
-//    the MFMAs (scheduling groups), so no memory instruction waits at issue
-//    behind a full queue with the matrix core idle.
-//  * The k-loop is free of branches: the slot freed by a stage is refilled
-//    with stage q of this tile or q - n_k of the next (a select), and past
-//    the last tile with a reload of the same tile that nothing reads, so the
-//    load count per stage, and with it every vmcnt wait, is the same always.
-//  * A ragged token tile still runs all MFMAs (rows past the count hold a
-//    clamped valid row and are not stored): every wave meets every barrier,
-//    so skipping a dead wave's MFMAs would not shorten the tile.
-template <int P, bool SWIGLU, typename TO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void wide_gemm_kernel(
-    const bf16_t *__restrict__ act, int64_t act_ld, const bf16_t *__restrict__ Wa,
-    const bf16_t *__restrict__ Wb, const int32_t *__restrict__ offsets, int E, int N, int K, int A,
-    TO *__restrict__ out) {
-    constexpr int BW = 256, BT = 256, kWaves = 4, kRows = BW + BT;
-    constexpr int LPW = kRows / 16 / kWaves;  // 16-row loads per wave per stage
-    constexpr int kStageBytes = kRows * 64;
-    constexpr int kCols = SWIGLU ? BW / 2 : BW;  // output columns per tile
-    constexpr int kKStep = 32;                   // bf16 K elements per stage
-    static_assert(LPW * (P - 1) < 64, "vmcnt range");
-    static_assert(P * kStageBytes <= 160 * 1024 - 1024, "LDS capacity");
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-    __shared__ int s_lo[64], s_cnt[64], s_first[65];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int n_tiles = (N + kCols - 1) / kCols;
-
-    if (tid == 0) {
-        int first = 0;
-        for (int i = 0; i < E; ++i) {
-            const int lo = min(max(offsets[i], 0), A);
-            const int hi = min(max(offsets[i + 1], lo), A);
-            s_lo[i] = lo;
-            s_cnt[i] = hi - lo;
-            s_first[i] = first;
-            first += (hi - lo + BT - 1) / BT * n_tiles;
-        }
-        s_first[E] = first;
-    }
-    __syncthreads();
-    const int total = s_first[E];
-
-    const int G8 = gridDim.x / 8;
-    const int xcd = blockIdx.x % 8, wj = blockIdx.x / 8;
-    const int range = (total + 7) / 8;
-    const int range_lo = xcd * range;
-    const int range_n = max(0, min(range, total - range_lo));
-    const int my_tiles = (range_n > wj) ? (range_n - wj + G8 - 1) / G8 : 0;
-    const int n_k = K / kKStep;  // >= P, checked by the launcher
-    if (my_tiles == 0) return;   // uniform over the workgroup
-
-    auto tile_info = [&](int k) {
-        const int t = range_lo + wj + k * G8;
-        int i = 0;
-        while (i + 1 < E && s_first[i + 1] <= t) ++i;
-        const int rem = t - s_first[i];
-        const int mtiles = (s_cnt[i] + BT - 1) / BT;
-        TileInfo ti;
-        ti.e = i;
-        ti.row0 = s_lo[i] + (rem % mtiles) * BT;
-        ti.mrem = min(BT, s_lo[i] + s_cnt[i] - ti.row0);
-        ti.n0 = (rem / mtiles) * kCols;
-        return ti;
-    };
-
-    // Lane pointers of this wave's LPW 16-row loads of a tile (same row and
-    // chunk assignment as grouped_gemm_kernel).
-    auto sources = [&](const TileInfo &ti, const char *(&src)[LPW]) {
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int r = (wave + kWaves * i) * 16 + (lane >> 2);
-            const int c = (lane & 3) ^ ((r >> 2) & 3);
-            if (r < BW) {
-                const bf16_t *W = Wa;
-                int nr;
-                if constexpr (SWIGLU) {
-                    W = (r < BW / 2) ? Wa : Wb;
-                    nr = ti.n0 + (r % (BW / 2));
-                } else {
-                    nr = ti.n0 + r;
-                }
-                nr = min(nr, N - 1);
-                src[i] = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + c * 16;
-            } else {
-                const int m = min(r - BW, ti.mrem - 1);
-                src[i] = (const char *)(act + (int64_t)(ti.row0 + m) * act_ld) + c * 16;
-            }
-        }
-    };
-
-    const int wn = wave & 1, wm = wave >> 1;
-    const int lrow = lane & 31, lhalf = lane >> 5;
-    // LDS row of weight fragment i (GEMM1: 0,1 are W1 rows, 2,3 the same W3 rows)
-    auto wrow = [&](int i) {
-        if constexpr (SWIGLU)
-            return (i < 2 ? 0 : BW / 2) + wn * 64 + (i & 1) * 32;
-        else
-            return wn * 128 + i * 32;
-    };
-    const int trow0 = BW + wm * 128;
-
-    f32x16 acc[4][4];
-    i32x4 a0[4], b0[4], a1[4], b1[4];
-    auto load_frags = [&](i32x4 (&a)[4], i32x4 (&b)[4], int slot, int t) {
-        const char *base = smem + slot * kStageBytes;
-        const int c = 2 * t + lhalf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *(const i32x4 *)(base + lds_off(wrow(i) + lrow, c));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = *(const i32x4 *)(base + lds_off(trow0 + j * 32 + lrow, c));
-    };
-    auto mma = [&](const i32x4 (&a)[4], const i32x4 (&b)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mma_step<bf16_t>(a[i], b[j], acc[i][j]);
-    };
-
-    const char *sc[LPW], *sn[LPW];  // sources of the current and the next tile
-    TileInfo nxt = tile_info(0);
-    sources(nxt, sn);
-#pragma unroll
-    for (int g = 0; g < P; ++g) {
-        char *dst = smem + g * kStageBytes;
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) dma16(sn[i] + g * 64, dst + (wave + kWaves * i) * 1024);
-    }
-    wait_vmcnt_lgkm0<LPW * (P - 1)>();
-    stage_barrier();
-    load_frags(a0, b0, 0, 0);
-
-    int g = 0;  // stages consumed so far = ring cursor
-    for (int c_k = 0; c_k < my_tiles; ++c_k) {
-        const TileInfo cur = nxt;
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) sc[i] = sn[i];
-        if (c_k + 1 < my_tiles) {
-            nxt = tile_info(c_k + 1);
-            sources(nxt, sn);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-        // Only fragment reads are pending inside the k-loop; a clean count
-        // here lets the compiler's own waits stay exact.
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-
-        for (int s = 0; s < n_k; ++s, ++g) {
-            const int slot = g % P;
-            // Second k-half of this stage, under the MFMAs of the first.
-            __builtin_amdgcn_sched_barrier(0);
-            load_frags(a1, b1, slot, 1);
-            mma(a0, b0);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            // Next stage landed (this wave's loads, then everyone's), and
-            // every wave is done reading this slot.
-            wait_vmcnt_lgkm0<LPW * (P - 2)>();
-            stage_barrier();
-            // Refill this slot P stages ahead; read the next stage's first
-            // k-half; both under the MFMAs of this stage's second half.
-            const int q = s + P;
-            const bool here = q < n_k;
-            const int64_t off = (int64_t)(here ? q : q - n_k) * 64;
-            char *dst = smem + slot * kStageBytes;
-            load_frags(a0, b0, (g + 1) % P, 0);
-#pragma unroll
-            for (int i = 0; i < LPW; ++i)
-                dma16((here ? sc[i] : sn[i]) + off, dst + (wave + kWaves * i) * 1024);
-            mma(a1, b1);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global->LDS load
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // The reads above were issued before eight MFMAs and have landed;
-            // saying so keeps the compiler's next wait at the next eight.
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        }
-
-        // Epilogue: element q of fragment (i, j) is D[n = 8 (q / 4) + 4 lhalf
-        // + q % 4][m = lrow]; GEMM1 pairs u fragment i with v fragment i + 2.
-        constexpr int NI = SWIGLU ? 2 : 4;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // Pin the fragment(s) in accumulator registers up to here, so
-                // they are moved out one fragment at a time, not all 256 at
-                // the loop exit.
-                asm volatile("" : "+a"(acc[i][j]));
-                if constexpr (SWIGLU) asm volatile("" : "+a"(acc[i + 2][j]));
-                const int m = wm * 128 + j * 32 + lrow;
-                if (m < cur.mrem) {
-                    TO *orow = out + (int64_t)(cur.row0 + m) * N;
-#pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        const int n = cur.n0 + (SWIGLU ? wn * 64 : wn * 128) + i * 32 + 8 * gq +
-                                      4 * lhalf;
-                        if (n < N) {
-                            float v[4];
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                v[q] = acc[i][j][4 * gq + q];
-                                if constexpr (SWIGLU) v[q] = silu(v[q]) * acc[i + 2][j][4 * gq + q];
-                            }
-                            store4<TO>(orow + n, v[0], v[1], v[2], v[3]);
-                        }
-                    }
-                }
-                // one fragment at a time: keeps the scheduler from reading
-                // every accumulator out at once
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    }
-    wait_vmcnt_lgkm0<0>();  // the trailing reloads land before the wave ends
-}
-
-static int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        return 256;
-    return cus;
-}
 
 template <int BW, int BT, int WN, int WM, int P, bool SWIGLU, typename T, typename TO = T>
 static hipError_t launch_grouped(const void *act, int64_t act_ld, const void *Wa, const void *Wb,
@@ -633,53 +298,43 @@ static hipError_t launch_grouped(const void *act, int64_t act_ld, const void *Wa
     return hipGetLastError();
 }
 
-template <int P, bool SWIGLU, typename TO>
-static hipError_t launch_wide(const void *act, int64_t act_ld, const void *Wa, const void *Wb,
-                              const int32_t *offsets, int E, int N, int K, int64_t A, void *out,
-                              hipStream_t s) {
-    auto kern = wide_gemm_kernel<P, SWIGLU, TO>;
-    constexpr int kLds = P * 512 * 64;
-    hipError_t err =
-        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (err != hipSuccess) return err;
-    const int64_t kCols = SWIGLU ? 128 : 256;
-    const int64_t n_tiles = (N + kCols - 1) / kCols;
-    const int64_t tile_bound = n_tiles * ((A + 255) / 256 + E - 1);
-    int64_t grid = device_cus();
-    grid = std::min<int64_t>(grid, (tile_bound + 7) / 8 * 8);
-    grid = std::max<int64_t>(8, grid / 8 * 8);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), kLds, s, (const bf16_t *)act, act_ld,
-                       (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
-                       (TO *)out);
-    return hipGetLastError();
+// Which kernels run the experts: decode-sized batches stream the weights
+// (skinny_gemm.hip), mid-sized ones use 8-wave grouped tiles, large bf16
+// ones the wide tiles (wide_gemm.hip).
+enum class FfnPath { kSkinny, kGroupedSmall, kGroupedLarge, kWide };
+
+static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
+    const int64_t per_expert = A / E;
+    if (per_expert <= 32) return FfnPath::kSkinny;
+    if (per_expert <= 256) return FfnPath::kGroupedSmall;
+    if (dt == 1 && wide_supported(d, d_ff)) return FfnPath::kWide;
+    return FfnPath::kGroupedLarge;
 }
 
 template <typename T, typename TO>
 static hipError_t launch_ffn_typed(const void *act, const int32_t *offsets, const void *W1,
                                    const void *W3, const void *W2, int64_t A, int d, int d_ff,
-                                   int E, void *hbuf, void *out, hipEvent_t mid, hipStream_t s) {
+                                   int E, void *hbuf, void *out, void *scratch,
+                                   size_t scratch_bytes, hipEvent_t mid, hipStream_t s) {
     hipError_t err;
-    const int64_t per_expert = A / E;
-    if (per_expert <= 32)  // decode-sized: a weight stream, see skinny_gemm.hip
-        return moe_launch_skinny_ffn(act, offsets, W1, W3, W2, ElemSize<T>::value == 4 ? 0 : 1,
-                                     ElemSize<TO>::value == 4, A, d, d_ff, E, hbuf, out, mid, s);
-    if (per_expert <= 256) {
-        err = launch_grouped<128, 64, 2, 2, 6, true, T>(act, d, W1, W3, offsets, E, d_ff, d, A,
-                                                         hbuf, 2, s);
-        if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
-        if (err != hipSuccess) return err;
-        return launch_grouped<128, 64, 2, 2, 6, false, T, TO>(hbuf, d_ff, W2, nullptr, offsets,
-                                                               E, d, d_ff, A, out, 2, s);
-    }
-    if constexpr (ElemSize<T>::value == 2) {
-        // bf16 with at least four 32-wide k-steps per tile: wide tiles
-        if (d >= 4 * 32 && d_ff >= 4 * 32) {
-            err = launch_wide<4, true, bf16_t>(act, d, W1, W3, offsets, E, d_ff, d, A, hbuf, s);
+    const int dt = ElemSize<T>::value == 4 ? 0 : 1;
+    switch (ffn_path(dt, A, d, d_ff, E)) {
+        case FfnPath::kSkinny:
+            return moe_launch_skinny_ffn(act, offsets, W1, W3, W2, dt, ElemSize<TO>::value == 4, A,
+                                         d, d_ff, E, hbuf, out, mid, s);
+        case FfnPath::kGroupedSmall:
+            err = launch_grouped<128, 64, 2, 2, 6, true, T>(act, d, W1, W3, offsets, E, d_ff, d,
+                                                             A, hbuf, 2, s);
             if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
             if (err != hipSuccess) return err;
-            return launch_wide<4, false, TO>(hbuf, d_ff, W2, nullptr, offsets, E, d, d_ff, A, out,
-                                             s);
-        }
+            return launch_grouped<128, 64, 2, 2, 6, false, T, TO>(hbuf, d_ff, W2, nullptr,
+                                                                   offsets, E, d, d_ff, A, out, 2,
+                                                                   s);
+        case FfnPath::kWide:
+            return launch_wide_ffn(act, offsets, W1, W3, W2, ElemSize<TO>::value == 4, A, d, d_ff,
+                                   E, hbuf, out, (float *)scratch, scratch_bytes, mid, s);
+        case FfnPath::kGroupedLarge:
+            break;
     }
     err = launch_grouped<256, 256, 4, 2, 4, true, T>(act, d, W1, W3, offsets, E, d_ff, d, A,
                                                       hbuf, 1, s);
@@ -691,17 +346,22 @@ static hipError_t launch_ffn_typed(const void *act, const int32_t *offsets, cons
 
 }  // namespace moe
 
+size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E) {
+    if (moe::ffn_path(dt, A, d, d_ff, E) != moe::FfnPath::kWide) return 0;
+    return moe::wide_partial_bytes();
+}
+
 hipError_t moe_launch_expert_ffn(const void *act, const int32_t *offsets, const void *W1,
                                  const void *W3, const void *W2, int dt, int out_f32, int64_t A,
-                                 int d, int d_ff, int E, void *hbuf, void *out, hipEvent_t mid,
-                                 hipStream_t s) {
+                                 int d, int d_ff, int E, void *hbuf, void *out, void *scratch,
+                                 size_t scratch_bytes, hipEvent_t mid, hipStream_t s) {
     using moe::bf16_t;
     if (dt == 0)
         return moe::launch_ffn_typed<float, float>(act, offsets, W1, W3, W2, A, d, d_ff, E, hbuf,
-                                                   out, mid, s);
+                                                   out, scratch, scratch_bytes, mid, s);
     if (out_f32)
         return moe::launch_ffn_typed<bf16_t, float>(act, offsets, W1, W3, W2, A, d, d_ff, E,
-                                                    hbuf, out, mid, s);
+                                                    hbuf, out, scratch, scratch_bytes, mid, s);
     return moe::launch_ffn_typed<bf16_t, bf16_t>(act, offsets, W1, W3, W2, A, d, d_ff, E, hbuf,
-                                                 out, mid, s);
+                                                 out, scratch, scratch_bytes, mid, s);
 }

@@ -1,0 +1,111 @@
+// gemm_common.h — device helpers shared by the expert GEMM kernels
+// (expert_gemm.hip, wide_gemm.hip): MFMA steps, output stores, explicit
+// waits, the fence-free barrier, global-to-LDS loads and the swizzled LDS
+// layout of a stage.
+#pragma once
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+
+template <typename T>
+struct ElemSize;
+template <>
+struct ElemSize<float> {
+    static constexpr int value = 4;
+};
+template <>
+struct ElemSize<bf16_t> {
+    static constexpr int value = 2;
+};
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// acc += A_frag * B_frag over one 32-byte k-step: 32 rows x 32 cols.
+template <typename T>
+__device__ __forceinline__ f32x16 mma_step(i32x4 a, i32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mma_step<bf16_t>(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mma_step<float>(i32x4 a, i32x4 b, f32x16 c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.x), __int_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.y), __int_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.z), __int_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.w), __int_as_float(b.w), c, 0, 0, 0);
+    return c;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T *out, float v0, float v1, float v2, float v3);
+
+template <>
+__device__ __forceinline__ void store4<float>(float *out, float v0, float v1, float v2,
+                                              float v3) {
+    *(float4 *)out = make_float4(v0, v1, v2, v3);
+}
+
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t *out, float v0, float v1, float v2,
+                                               float v3) {
+    *(uint2 *)out = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+}
+
+__device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
+
+// s_waitcnt constraining vmcnt to N and lgkmcnt to 0 (expcnt free); gfx9
+// encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier without a memory fence: the explicit waits decide what
+// has landed in LDS; the empty asm statements and scheduling barriers keep
+// the compiler from moving memory operations across it.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const char *g, char *lds) {
+    __builtin_amdgcn_global_load_lds((const void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Byte offset of 16-byte chunk c of LDS row r within a stage.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+struct TileInfo {
+    int e, row0, mrem, n0;
+};
+
+static inline int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    return cus;
+}
+
+// Wide-tile expert GEMMs (wide_gemm.hip), bf16 only.  `partial` (may be
+// NULL) is scratch for split tiles, at least wide_partial_bytes() bytes.
+size_t wide_partial_bytes();
+bool wide_supported(int d, int d_ff);
+hipError_t launch_wide_ffn(const void *act, const int32_t *offsets, const void *W1,
+                           const void *W3, const void *W2, int out_f32, int64_t A, int d,
+                           int d_ff, int E, void *hbuf, void *out, float *partial,
+                           size_t partial_bytes, hipEvent_t mid, hipStream_t s);
+
+}  // namespace moe
