@@ -299,13 +299,15 @@ static hipError_t launch_grouped(const void *act, int64_t act_ld, const void *Wa
 }
 
 // Which kernels run the experts: decode-sized batches stream the weights
-// (skinny_gemm.hip), mid-sized ones use 8-wave grouped tiles, large bf16
-// ones the wide tiles (wide_gemm.hip).
-enum class FfnPath { kSkinny, kGroupedSmall, kGroupedLarge, kWide };
+// (stream_gemm.hip for bf16, skinny_gemm.hip for fp32 or small d), mid-sized
+// ones use 8-wave grouped tiles, large bf16 ones the wide tiles
+// (wide_gemm.hip).
+enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide };
 
 static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
     const int64_t per_expert = A / E;
-    if (per_expert <= 32) return FfnPath::kSkinny;
+    if (per_expert <= 32)
+        return (dt == 1 && stream_supported(d, d_ff)) ? FfnPath::kStream : FfnPath::kSkinny;
     if (per_expert <= 256) return FfnPath::kGroupedSmall;
     if (dt == 1 && wide_supported(d, d_ff)) return FfnPath::kWide;
     return FfnPath::kGroupedLarge;
@@ -319,6 +321,9 @@ static hipError_t launch_ffn_typed(const void *act, const int32_t *offsets, cons
     hipError_t err;
     const int dt = ElemSize<T>::value == 4 ? 0 : 1;
     switch (ffn_path(dt, A, d, d_ff, E)) {
+        case FfnPath::kStream:
+            return launch_stream_ffn(act, offsets, W1, W3, W2, ElemSize<TO>::value == 4, A, d,
+                                     d_ff, E, hbuf, out, mid, s);
         case FfnPath::kSkinny:
             return moe_launch_skinny_ffn(act, offsets, W1, W3, W2, dt, ElemSize<TO>::value == 4, A,
                                          d, d_ff, E, hbuf, out, mid, s);

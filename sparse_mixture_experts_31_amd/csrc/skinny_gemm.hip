@@ -89,7 +89,23 @@ struct SkinnyCfg {
     static_assert(TN >= 1 && TM >= 1, "wave tile too small");
     static_assert(BN % (WN * 16) == 0 && BM % (WM * 16) == 0, "tile shape");
     static_assert(kLdsBytes <= 64 * 1024, "static LDS");
+    static_assert(kWRows * 8 % kThreads == 0, "a thread's chunk i is all weight or all token rows");
+    // chunks [0, NW) of every thread hold weight rows, the rest token rows
+    static constexpr int NW = kWRows * 8 / kThreads;
 };
+
+// Weight chunks are read once per call: non-temporal loads stream them past
+// the caches, which lifts the sustained HBM read rate (measured on MI355X:
+// about 7 TB/s against about 6.2 TB/s for plain loads).  Token rows are
+// shared by every tile of an expert and keep the default policy.
+template <int CPT, int NW>
+__device__ __forceinline__ void load_stage(i32x4 (&regs)[CPT], const char *const (&src)[CPT],
+                                           int64_t off) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) regs[i] = __builtin_nontemporal_load((const i32x4 *)(src[i] + off));
+#pragma unroll
+    for (int i = NW; i < CPT; ++i) regs[i] = *(const i32x4 *)(src[i] + off);
+}
 
 // T: activation and weight type; TO: output type (T, or fp32 for the expert
 // outputs the fused layer combines).
@@ -171,19 +187,14 @@ __global__ __launch_bounds__(WN *WM *kWave) void skinny_gemm_kernel(
     const int n_stages = K / C::kKStep;
 
     i32x4 regs[CPT];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) regs[i] = *(const i32x4 *)src[i];
+    load_stage<CPT, C::NW>(regs, src, 0);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) *(i32x4 *)(smem + dst[i]) = regs[i];
     __syncthreads();
 
     for (int s = 0; s < n_stages; ++s) {
         const int buf = s & 1;
-        if (s + 1 < n_stages) {
-#pragma unroll
-            for (int i = 0; i < CPT; ++i)
-                regs[i] = *(const i32x4 *)(src[i] + (int64_t)(s + 1) * 128);
-        }
+        if (s + 1 < n_stages) load_stage<CPT, C::NW>(regs, src, (int64_t)(s + 1) * 128);
         const char *sW = smem + buf * C::kStageBytes;
         const char *sX = sW + C::kWRows * 128;
 #pragma unroll

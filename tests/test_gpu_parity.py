@@ -169,10 +169,15 @@ def test_pieces_expert_ffn_and_combine():
     assert normwise(to_np(y2), want_y + to_np(res)) < 4e-3
 
 
-def test_all_tokens_to_two_experts_and_untouched_experts():
+@pytest.mark.parametrize("w", [
+    Workload("forced", 20, T=200, d=256, d_ff=512),
+    # decode-sized (T*k/E <= 32): the weight-streaming kernels, here with two
+    # token tiles for each of the two experts
+    Workload("forced-stream", 21, T=128, d=384, d_ff=768),
+], ids=lambda w: w.name)
+def test_all_tokens_to_two_experts_and_untouched_experts(w):
     """Every token routes to experts 3 and 5; the other six get no rows, and
     NaN in their weights must not reach y (their parameters are not read)."""
-    w = Workload("forced", 20, T=200, d=256, d_ff=512)
     L = _case(w)
     Wg = torch.zeros_like(L["Wg"])
     Wg[3, 0] = 10.0
