@@ -189,7 +189,8 @@ moe_status moe_expert_ffn(const void *x_perm, const int32_t *offsets, const void
     if (!ws || ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
     REQUIRE_PTR(ws, kAlign);
-    LAUNCH(moe_launch_expert_ffn(x_perm, offsets, W1, W3, W2, (int)dt, 0, T * k, d, d_ff, E, ws,
+    LAUNCH(moe_launch_expert_ffn(x_perm, nullptr, offsets, W1, W3, W2, (int)dt, 0, T * k, d,
+                                 d_ff, E, ws,
                                  out_perm, split_bytes ? at<char>(ws, h_bytes) : nullptr,
                                  split_bytes, nullptr, (hipStream_t)stream),
            "expert_ffn");
@@ -236,14 +237,18 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
     LAUNCH(mark(1), "event");
     LAUNCH(moe_launch_dispatch_index(idx, A, E, k, counts, offsets, row_of, token_of, s),
            "dispatch");
-    // The expert GEMMs read contiguous rows: copy each token's row to its k
-    // places in expert order first.
-    LAUNCH(moe_launch_gather_rows(x, (int)dt, T, d, k, row_of, x_perm, s), "gather");
+    // The large-tile and weight-streaming expert kernels read each token's
+    // row in place through token_of; the others read rows in expert order,
+    // so copy each token's row to its k places first.
+    const bool gathers = moe_expert_ffn_gathers((int)dt, A, d, d_ff, E);
+    if (!gathers)
+        LAUNCH(moe_launch_gather_rows(x, (int)dt, T, d, k, row_of, x_perm, s), "gather");
     LAUNCH(mark(2), "event");
     // The W2 GEMM leaves the expert outputs in fp32; the combine rounds once.
-    LAUNCH(moe_launch_expert_ffn(x_perm, offsets, W1, W3, W2, (int)dt, 1, A, d, d_ff, E, hbuf,
-                                 o_perm, c.split_bytes ? at<char>(ws, c.split) : nullptr,
-                                 c.split_bytes, ev ? (hipEvent_t)ev[3] : nullptr, s),
+    LAUNCH(moe_launch_expert_ffn(gathers ? x : x_perm, gathers ? token_of : nullptr, offsets, W1,
+                                 W3, W2, (int)dt, 1, A, d, d_ff, E, hbuf, o_perm,
+                                 c.split_bytes ? at<char>(ws, c.split) : nullptr, c.split_bytes,
+                                 ev ? (hipEvent_t)ev[3] : nullptr, s),
            "expert_ffn");
     LAUNCH(mark(4), "event");
     LAUNCH(moe_launch_combine(o_perm, 1, row_of, gw, residual, (int)dt, T, d, k, y, s),

@@ -70,11 +70,16 @@ hipError_t moe_launch_gather_rows(const void *x, int dt, int64_t T, int d, int k
 // `mid_event` (may be NULL) is recorded between the W1/W3 GEMM and the W2 GEMM.
 // `out_f32` != 0: the W2 GEMM writes fp32 expert outputs instead of dt.
 // `scratch` (may be NULL) holds partial sums of split tiles, at least
-// moe_expert_ffn_scratch_bytes() bytes to be used.
-hipError_t moe_launch_expert_ffn(const void *act, const int32_t *offsets, const void *W1,
-                                 const void *W3, const void *W2, int dt, int out_f32, int64_t A,
-                                 int d, int d_ff, int E, void *hbuf, void *out, void *scratch,
-                                 size_t scratch_bytes, hipEvent_t mid_event, hipStream_t s);
+// moe_expert_ffn_scratch_bytes() bytes to be used.  `gather` NULL: act is
+// x_perm (rows in expert order); else act is x and expert-order row r is
+// x[gather[r]] (token_of), which the kernels of a shape support only if
+// moe_expert_ffn_gathers() says so (else hipErrorInvalidValue).
+hipError_t moe_launch_expert_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
+                                 const void *W1, const void *W3, const void *W2, int dt,
+                                 int out_f32, int64_t A, int d, int d_ff, int E, void *hbuf,
+                                 void *out, void *scratch, size_t scratch_bytes,
+                                 hipEvent_t mid_event, hipStream_t s);
+bool moe_expert_ffn_gathers(int dt, int64_t A, int d, int d_ff, int E);
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E);
 // The same experts for decode-sized batches (few rows per expert).
 hipError_t moe_launch_skinny_ffn(const void *x_perm, const int32_t *offsets, const void *W1,

@@ -313,17 +313,22 @@ static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
     return FfnPath::kGroupedLarge;
 }
 
+static bool path_gathers(FfnPath p) { return p == FfnPath::kStream || p == FfnPath::kWide; }
+
 template <typename T, typename TO>
-static hipError_t launch_ffn_typed(const void *act, const int32_t *offsets, const void *W1,
-                                   const void *W3, const void *W2, int64_t A, int d, int d_ff,
-                                   int E, void *hbuf, void *out, void *scratch,
-                                   size_t scratch_bytes, hipEvent_t mid, hipStream_t s) {
+static hipError_t launch_ffn_typed(const void *act, const int32_t *gather,
+                                   const int32_t *offsets, const void *W1, const void *W3,
+                                   const void *W2, int64_t A, int d, int d_ff, int E, void *hbuf,
+                                   void *out, void *scratch, size_t scratch_bytes,
+                                   hipEvent_t mid, hipStream_t s) {
     hipError_t err;
     const int dt = ElemSize<T>::value == 4 ? 0 : 1;
-    switch (ffn_path(dt, A, d, d_ff, E)) {
+    const FfnPath path = ffn_path(dt, A, d, d_ff, E);
+    if (gather && !path_gathers(path)) return hipErrorInvalidValue;
+    switch (path) {
         case FfnPath::kStream:
-            return launch_stream_ffn(act, offsets, W1, W3, W2, ElemSize<TO>::value == 4, A, d,
-                                     d_ff, E, hbuf, out, mid, s);
+            return launch_stream_ffn(act, gather, offsets, W1, W3, W2, ElemSize<TO>::value == 4,
+                                     A, d, d_ff, E, hbuf, out, mid, s);
         case FfnPath::kSkinny:
             return moe_launch_skinny_ffn(act, offsets, W1, W3, W2, dt, ElemSize<TO>::value == 4, A,
                                          d, d_ff, E, hbuf, out, mid, s);
@@ -336,8 +341,9 @@ static hipError_t launch_ffn_typed(const void *act, const int32_t *offsets, cons
                                                                    offsets, E, d, d_ff, A, out, 2,
                                                                    s);
         case FfnPath::kWide:
-            return launch_wide_ffn(act, offsets, W1, W3, W2, ElemSize<TO>::value == 4, A, d, d_ff,
-                                   E, hbuf, out, (float *)scratch, scratch_bytes, mid, s);
+            return launch_wide_ffn(act, gather, offsets, W1, W3, W2, ElemSize<TO>::value == 4, A,
+                                   d, d_ff, E, hbuf, out, (float *)scratch, scratch_bytes, mid,
+                                   s);
         case FfnPath::kGroupedLarge:
             break;
     }
@@ -351,22 +357,27 @@ static hipError_t launch_ffn_typed(const void *act, const int32_t *offsets, cons
 
 }  // namespace moe
 
+bool moe_expert_ffn_gathers(int dt, int64_t A, int d, int d_ff, int E) {
+    return moe::path_gathers(moe::ffn_path(dt, A, d, d_ff, E));
+}
+
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E) {
     if (moe::ffn_path(dt, A, d, d_ff, E) != moe::FfnPath::kWide) return 0;
     return moe::wide_partial_bytes();
 }
 
-hipError_t moe_launch_expert_ffn(const void *act, const int32_t *offsets, const void *W1,
-                                 const void *W3, const void *W2, int dt, int out_f32, int64_t A,
-                                 int d, int d_ff, int E, void *hbuf, void *out, void *scratch,
-                                 size_t scratch_bytes, hipEvent_t mid, hipStream_t s) {
+hipError_t moe_launch_expert_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
+                                 const void *W1, const void *W3, const void *W2, int dt,
+                                 int out_f32, int64_t A, int d, int d_ff, int E, void *hbuf,
+                                 void *out, void *scratch, size_t scratch_bytes, hipEvent_t mid,
+                                 hipStream_t s) {
     using moe::bf16_t;
     if (dt == 0)
-        return moe::launch_ffn_typed<float, float>(act, offsets, W1, W3, W2, A, d, d_ff, E, hbuf,
-                                                   out, scratch, scratch_bytes, mid, s);
+        return moe::launch_ffn_typed<float, float>(act, gather, offsets, W1, W3, W2, A, d, d_ff,
+                                                   E, hbuf, out, scratch, scratch_bytes, mid, s);
     if (out_f32)
-        return moe::launch_ffn_typed<bf16_t, float>(act, offsets, W1, W3, W2, A, d, d_ff, E,
-                                                    hbuf, out, scratch, scratch_bytes, mid, s);
-    return moe::launch_ffn_typed<bf16_t, bf16_t>(act, offsets, W1, W3, W2, A, d, d_ff, E, hbuf,
-                                                 out, scratch, scratch_bytes, mid, s);
+        return moe::launch_ffn_typed<bf16_t, float>(act, gather, offsets, W1, W3, W2, A, d, d_ff,
+                                                    E, hbuf, out, scratch, scratch_bytes, mid, s);
+    return moe::launch_ffn_typed<bf16_t, bf16_t>(act, gather, offsets, W1, W3, W2, A, d, d_ff, E,
+                                                 hbuf, out, scratch, scratch_bytes, mid, s);
 }

@@ -92,6 +92,28 @@ __device__ __forceinline__ void dma16_nt(const char *g, char *lds) {
                                      2 /* nt */);
 }
 
+// Activation row of the expert-order rows rb + lane / (64 / ROWS) (the rows
+// one load instruction covers), rows past `last` repeating `last`.  With a
+// gather map (the token of each expert-order row) the rows are the tokens'
+// own rows, read in place instead of from a gathered copy.  The map is read
+// with wave-uniform addresses through the scalar cache: those loads count on
+// lgkmcnt, so they never wait behind the vector-memory loads of a ring in
+// flight (vmcnt retires in issue order).
+template <int ROWS>
+__device__ __forceinline__ int act_row(const int32_t *__restrict__ gather, int rb, int last,
+                                       int lane) {
+    const int own = min(rb + lane / (64 / ROWS), last);
+    if (!gather) return own;
+    int v = 0;
+#pragma unroll
+    for (int q = 0; q < ROWS; ++q) {
+        const int r = __builtin_amdgcn_readfirstlane(min(rb + q, last));
+        const int t = __builtin_amdgcn_readfirstlane(gather[r]);
+        v = (lane == q) ? t : v;
+    }
+    return __shfl(v, lane / (64 / ROWS));
+}
+
 // Byte offset of 16-byte chunk c of LDS row r within a stage.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
@@ -111,18 +133,18 @@ static inline int device_cus() {
 // Weight-streaming expert GEMMs for decode-sized bf16 batches
 // (stream_gemm.hip).
 bool stream_supported(int d, int d_ff);
-hipError_t launch_stream_ffn(const void *act, const int32_t *offsets, const void *W1,
-                             const void *W3, const void *W2, int out_f32, int64_t A, int d,
-                             int d_ff, int E, void *hbuf, void *out, hipEvent_t mid,
-                             hipStream_t s);
+hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
+                             const void *W1, const void *W3, const void *W2, int out_f32,
+                             int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
+                             hipEvent_t mid, hipStream_t s);
 
 // Wide-tile expert GEMMs (wide_gemm.hip), bf16 only.  `partial` (may be
 // NULL) is scratch for split tiles, at least wide_partial_bytes() bytes.
 size_t wide_partial_bytes();
 bool wide_supported(int d, int d_ff);
-hipError_t launch_wide_ffn(const void *act, const int32_t *offsets, const void *W1,
-                           const void *W3, const void *W2, int out_f32, int64_t A, int d,
-                           int d_ff, int E, void *hbuf, void *out, float *partial,
+hipError_t launch_wide_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
+                           const void *W1, const void *W3, const void *W2, int out_f32, int64_t A,
+                           int d, int d_ff, int E, void *hbuf, void *out, float *partial,
                            size_t partial_bytes, hipEvent_t mid, hipStream_t s);
 
 }  // namespace moe

@@ -54,9 +54,9 @@ static_assert(kSLds <= 160 * 1024 - 1024, "LDS capacity");
 
 template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(
-    const bf16_t *__restrict__ act, int64_t act_ld, const bf16_t *__restrict__ Wa,
-    const bf16_t *__restrict__ Wb, const int32_t *__restrict__ offsets, int E, int N, int K, int A,
-    TO *__restrict__ out) {
+    const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ gather,
+    const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb,
+    const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out) {
     constexpr int P = kSP, LPW = kSLPW, BW = kSBW, BT = kSBT;
     constexpr int kCols = SWIGLU ? BW / 2 : BW;  // output columns per tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
 
     // Lane pointers of this wave's LPW 8-row loads: load i covers stage rows
     // (wave + 4 i) * 8 .. + 8, lane l the chunk that belongs at LDS offset
-    // 16 l; loads [0, kSWLoads) are weight rows.
+    // 16 l; loads [0, kSWLoads) are weight rows, the rest token rows (act
+    // rows, through `gather` if set).
     auto sources = [&](const TileInfo &ti, const char *(&src)[LPW]) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
@@ -122,8 +123,9 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
                 nr = min(nr, N - 1);
                 src[i] = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + c * 16;
             } else {
-                const int m = min(r - BW, ti.mrem - 1);
-                src[i] = (const char *)(act + (int64_t)(ti.row0 + m) * act_ld) + c * 16;
+                const int row = act_row<8>(gather, ti.row0 + (wave + kSWaves * i) * 8 - BW,
+                                           ti.row0 + ti.mrem - 1, lane);
+                src[i] = (const char *)(act + (int64_t)row * act_ld) + c * 16;
             }
         }
     };
@@ -215,9 +217,9 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
 namespace {
 
 template <bool SWIGLU, typename TO>
-hipError_t launch_stream(const void *act, int64_t act_ld, const void *Wa, const void *Wb,
-                         const int32_t *offsets, int E, int N, int K, int64_t A, void *out,
-                         hipStream_t s) {
+hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
+                         const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
+                         void *out, hipStream_t s) {
     auto kern = stream_gemm_kernel<SWIGLU, TO>;
     hipError_t err =
         hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kSLds);
@@ -228,7 +230,7 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const void *Wa, const 
     const int64_t tile_bound = (N + cols - 1) / cols * ((A + kSBT - 1) / kSBT + E - 1);
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), tile_bound));
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), kSLds, s, (const bf16_t *)act, act_ld,
-                       (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
+                       gather, (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
                        (TO *)out);
     return hipGetLastError();
 }
@@ -239,17 +241,19 @@ bool stream_supported(int d, int d_ff) {
     return d >= (kSP - 1) * kSKStep && d_ff >= (kSP - 1) * kSKStep;
 }
 
-hipError_t launch_stream_ffn(const void *act, const int32_t *offsets, const void *W1,
-                             const void *W3, const void *W2, int out_f32, int64_t A, int d,
-                             int d_ff, int E, void *hbuf, void *out, hipEvent_t mid,
-                             hipStream_t s) {
-    hipError_t err = launch_stream<true, bf16_t>(act, d, W1, W3, offsets, E, d_ff, d, A, hbuf, s);
+hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
+                             const void *W1, const void *W3, const void *W2, int out_f32,
+                             int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
+                             hipEvent_t mid, hipStream_t s) {
+    hipError_t err =
+        launch_stream<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A, hbuf, s);
     if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
     if (err != hipSuccess) return err;
     if (out_f32)
-        return launch_stream<false, float>(hbuf, d_ff, W2, nullptr, offsets, E, d, d_ff, A, out,
-                                           s);
-    return launch_stream<false, bf16_t>(hbuf, d_ff, W2, nullptr, offsets, E, d, d_ff, A, out, s);
+        return launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff,
+                                           A, out, s);
+    return launch_stream<false, bf16_t>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff, A,
+                                        out, s);
 }
 
 }  // namespace moe

@@ -156,9 +156,10 @@ __device__ __forceinline__ float *slot_ptr(float *partial, int slot) {
 
 template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void wide_gemm_kernel(
-    const bf16_t *__restrict__ act, int64_t act_ld, const bf16_t *__restrict__ Wa,
-    const bf16_t *__restrict__ Wb, const int32_t *__restrict__ offsets, int E, int N, int K, int A,
-    TO *__restrict__ out, float *__restrict__ partial) {
+    const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ gather,
+    const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb,
+    const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out,
+    float *__restrict__ partial) {
     constexpr int P = kWideP, LPW = kWideLPW, BW = kWideBW;
     constexpr int kCols = SWIGLU ? BW / 2 : BW;  // output columns per tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -204,13 +205,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // Lane pointers of this wave's LPW 16-row loads of a tile: row r of a
     // stage is loaded by wave (r / 16) % 4, lane 4 (r % 16) + chunk slot,
-    // fetching the chunk that belongs at that slot.
+    // fetching the chunk that belongs at that slot.  Loads [0, LPW / 2) are
+    // weight rows, the rest token rows (act rows, through `gather` if set).
     auto sources = [&](const TileInfo &ti, const char *(&src)[LPW]) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int r = (wave + kWideWaves * i) * 16 + (lane >> 2);
             const int c = (lane & 3) ^ ((r >> 2) & 3);
-            if (r < BW) {
+            if (i < LPW / 2) {
                 const bf16_t *W = Wa;
                 int nr;
                 if constexpr (SWIGLU) {
@@ -222,8 +224,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 nr = min(nr, N - 1);
                 src[i] = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + c * 16;
             } else {
-                const int m = min(r - BW, ti.mrem - 1);
-                src[i] = (const char *)(act + (int64_t)(ti.row0 + m) * act_ld) + c * 16;
+                const int row = act_row<16>(gather, ti.row0 + (wave + kWideWaves * i) * 16 - BW,
+                                            ti.row0 + ti.mrem - 1, lane);
+                src[i] = (const char *)(act + (int64_t)row * act_ld) + c * 16;
             }
         }
     };
@@ -446,16 +449,16 @@ namespace {
 int wide_grid() { return std::max(8, std::min(device_cus(), 512) / 8 * 8); }
 
 template <bool SWIGLU, typename TO>
-hipError_t launch_wide(const void *act, int64_t act_ld, const void *Wa, const void *Wb,
-                       const int32_t *offsets, int E, int N, int K, int64_t A, void *out,
-                       float *partial, hipStream_t s) {
+hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
+                       const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
+                       void *out, float *partial, hipStream_t s) {
     auto kern = wide_gemm_kernel<SWIGLU, TO>;
     hipError_t err = hipFuncSetAttribute((const void *)kern,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
     if (err != hipSuccess) return err;
     const int grid = wide_grid();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), kWideLds, s, (const bf16_t *)act, act_ld,
-                       (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
+                       gather, (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
                        (TO *)out, partial);
     if ((err = hipGetLastError()) != hipSuccess || !partial) return err;
     hipLaunchKernelGGL((wide_fixup_kernel<SWIGLU, TO>), dim3(grid), dim3(256), 0, s, offsets, E,
@@ -471,20 +474,20 @@ bool wide_supported(int d, int d_ff) {
     return d >= kWideP * kWideKStep && d_ff >= kWideP * kWideKStep;
 }
 
-hipError_t launch_wide_ffn(const void *act, const int32_t *offsets, const void *W1,
-                           const void *W3, const void *W2, int out_f32, int64_t A, int d,
-                           int d_ff, int E, void *hbuf, void *out, float *partial,
+hipError_t launch_wide_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
+                           const void *W1, const void *W3, const void *W2, int out_f32, int64_t A,
+                           int d, int d_ff, int E, void *hbuf, void *out, float *partial,
                            size_t partial_bytes, hipEvent_t mid, hipStream_t s) {
     if (partial && partial_bytes < wide_partial_bytes()) partial = nullptr;  // no splits
-    hipError_t err = launch_wide<true, bf16_t>(act, d, W1, W3, offsets, E, d_ff, d, A, hbuf,
-                                               partial, s);
+    hipError_t err = launch_wide<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A,
+                                               hbuf, partial, s);
     if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
     if (err != hipSuccess) return err;
     if (out_f32)
-        return launch_wide<false, float>(hbuf, d_ff, W2, nullptr, offsets, E, d, d_ff, A, out,
-                                         partial, s);
-    return launch_wide<false, bf16_t>(hbuf, d_ff, W2, nullptr, offsets, E, d, d_ff, A, out,
-                                      partial, s);
+        return launch_wide<false, float>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff,
+                                         A, out, partial, s);
+    return launch_wide<false, bf16_t>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff, A,
+                                      out, partial, s);
 }
 
 }  // namespace moe
