@@ -167,7 +167,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    // wave-uniform by construction; saying so keeps the LDS destinations of
+    // the loads (M0) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int n_k = K / kWideKStep;  // >= P, checked by the launcher
 
     TileTable tt{s_lo, s_cnt, s_first, E};
@@ -260,34 +262,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int j = 0; j < 4; ++j) acc[i][j] = mma_step<bf16_t>(a[i], b[j], acc[i][j]);
     };
 
-    const char *sc[LPW], *sn[LPW];  // sources of the current and the next segment's tile
-    Segment nxt = segment(0);
-    sources(tt.info(nxt.tile, kCols), sn);
-    // Every segment holds at least P stages (whole tiles have n_k >= P, split
-    // pieces are multiples of P), so the first P stages come from segment 0.
+    // The producer runs P stages ahead of the consumer with its own cursor:
+    // pp are its lane pointers into the next stage to load, p_left the
+    // stages left in its segment.  Every segment holds at least P stages
+    // (whole tiles n_k >= P, split pieces multiples of P).  Past the last
+    // segment it reloads the first stages of that segment, which nothing
+    // reads, so every stage issues the same loads.
+    const char *pp[LPW];
+    int p_left;
+    auto produce_from = [&](int k) {
+        const Segment sg = segment(min(k, n_seg - 1));
+        sources(tt.info(sg.tile, kCols), pp);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) pp[i] += (int64_t)sg.sb * 64;
+        p_left = (k < n_seg) ? sg.se - sg.sb : 0x7fffffff;
+    };
+    int p_seg = 0;
+    produce_from(0);
 #pragma unroll
     for (int g = 0; g < P; ++g) {
         char *dst = smem + g * kWideStageBytes;
 #pragma unroll
-        for (int i = 0; i < LPW; ++i)
-            dma16(sn[i] + (int64_t)(nxt.sb + g) * 64, dst + (wave + kWideWaves * i) * 1024);
+        for (int i = 0; i < LPW; ++i) {
+            dma16(pp[i], dst + (wave + kWideWaves * i) * 1024);
+            pp[i] += 64;
+        }
     }
+    p_left -= P;
+    if (p_left == 0) produce_from(++p_seg);
     wait_vmcnt_lgkm0<LPW * (P - 1)>();
     stage_barrier();
     load_frags(a0, b0, 0, 0);
 
     int g = 0;  // stages consumed so far = ring cursor
     for (int c_k = 0; c_k < n_seg; ++c_k) {
-        const Segment cur = nxt;
+        const Segment cur = segment(c_k);
         const TileInfo ti = tt.info(cur.tile, kCols);
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) sc[i] = sn[i];
-        if (c_k + 1 < n_seg) {
-            nxt = segment(c_k + 1);
-            sources(tt.info(nxt.tile, kCols), sn);
-        }
-        // (past the last segment nxt == cur and sn == sc: the refills below
-        // reload stages of this segment, which nothing reads)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -315,14 +325,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             stage_barrier();
             // Refill this slot P stages ahead; read the next stage's first
             // k-half; both under the MFMAs of this stage's second half.
-            const int q = s + P;
-            const bool here = q < cur.se;
-            const int64_t off = (int64_t)(here ? q : nxt.sb + q - cur.se) * 64;
             char *dst = smem + slot * kWideStageBytes;
             load_frags(a0, b0, (g + 1) % P, 0);
 #pragma unroll
-            for (int i = 0; i < LPW; ++i)
-                dma16((here ? sc[i] : sn[i]) + off, dst + (wave + kWideWaves * i) * 1024);
+            for (int i = 0; i < LPW; ++i) {
+                dma16(pp[i], dst + (wave + kWideWaves * i) * 1024);
+                pp[i] += 64;
+            }
             mma(a1, b1);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -338,6 +347,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             // The reads above were issued before eight MFMAs and have landed;
             // saying so keeps the compiler's next wait at the next eight.
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+            if (--p_left == 0) produce_from(++p_seg);  // the producer's next segment
         }
 
         if (cur.slot < 0) {
