@@ -389,7 +389,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // Sums the parts of every split tile in workgroup order and applies the
-// epilogue.  Block b handles tile b / 8 of the split round of XCD b % 8.
+// epilogue.  Block b handles fragment b % 16 (GEMM1: u/v pair b % 8; the
+// other eight blocks exit) of tile b / 128 of the split round of XCD
+// (b / 16) % 8: one fragment per block keeps many loads in flight.
 template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restrict__ offsets,
                                                          int E, int N, int K, int A, int G8,
@@ -401,7 +403,8 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
     const int tid = threadIdx.x;
     const int n_k = K / kWideKStep;
     TileTable tt{s_lo, s_cnt, s_first, E};
-    const int xcd = blockIdx.x % 8, jr = blockIdx.x / 8;
+    const int frag = blockIdx.x % 16, xcd = (blockIdx.x / 16) % 8, jr = blockIdx.x / 128;
+    if (SWIGLU && frag >= 8) return;
     if (tid == 0) {
         tt.build(offsets, A, (N + kCols - 1) / kCols);
         const XcdShare xs(tt.total(), xcd, G8, n_k, n_k % kWideP == 0);
@@ -430,6 +433,7 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
     const int wn = wave & 1, wm = wave >> 1;
     auto load_sum = [&](int i, int j) {
         f32x16 r{};
+#pragma unroll 4
         for (int k = 0; k < np; ++k) {
             const float *src = partial + (size_t)s_slots[k] * kSlotFloats;
 #pragma unroll
@@ -444,13 +448,11 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
         }
         return r;
     };
-    constexpr int NI = SWIGLU ? 2 : 4;
-    for (int i = 0; i < NI; ++i)
-        for (int j = 0; j < 4; ++j) {
-            const f32x16 u = load_sum(i, j);
-            const f32x16 v = SWIGLU ? load_sum(i + 2, j) : u;
-            store_fragment<SWIGLU, TO>(out, N, ti, wn, wm, lane, i, j, u, v);
-        }
+    // GEMM1: u/v fragment pair (i, j), i < 2; GEMM2: fragment (i, j)
+    const int i = frag / 4, j = frag % 4;
+    const f32x16 u = load_sum(i, j);
+    const f32x16 v = SWIGLU ? load_sum(i + 2, j) : u;
+    store_fragment<SWIGLU, TO>(out, N, ti, wn, wm, lane, i, j, u, v);
 }
 
 namespace {
@@ -471,8 +473,8 @@ hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, c
                        gather, (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
                        (TO *)out, partial);
     if ((err = hipGetLastError()) != hipSuccess || !partial) return err;
-    hipLaunchKernelGGL((wide_fixup_kernel<SWIGLU, TO>), dim3(grid), dim3(256), 0, s, offsets, E,
-                       N, K, (int)A, grid / 8, (TO *)out, (const float *)partial);
+    hipLaunchKernelGGL((wide_fixup_kernel<SWIGLU, TO>), dim3(grid * 16), dim3(256), 0, s, offsets,
+                       E, N, K, (int)A, grid / 8, (TO *)out, (const float *)partial);
     return hipGetLastError();
 }
 
