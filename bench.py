@@ -138,6 +138,43 @@ def cpu_baseline(w, L, budget_tokens, budget_s=10.0):
                       f"{elapsed:.1f} s wall on {threads} threads"}
 
 
+def decode_sweep(w, L, moe, np, torch, stream, steps):
+    """The decode layer at T = 1, 2, 4, 8, 16 tokens (the first T rows of the
+    batch, same weights): time per layer, the experts the batch activates and
+    the HBM rate of reading their weights.  Only active experts are read, so
+    the bytes grow with T until all eight are in use."""
+    res = {}
+    ev = torch.cuda.Event
+    for T in (1, 2, 4, 8, 16):
+        x = L["x"][:T].contiguous()
+        ws = moe.workspace(T, w.d, w.d_ff, w.E, w.k, x.dtype, x.device)
+        y = torch.empty_like(x)
+
+        def run():
+            moe.moe_forward(x, L["Wg"], L["W1"], L["W3"], L["W2"], w.k, y=y, ws=ws,
+                            stream=stream)
+
+        for _ in range(3):
+            run()
+        a, b = ev(enable_timing=True), ev(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        idx, _ = moe.moe_route(x, L["Wg"], w.k)
+        n_active = int((np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.E) > 0).sum())
+        wbytes = n_active * 3 * w.d * w.d_ff * 2
+        res[str(T)] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                       "active_experts": n_active,
+                       "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        print(f"[bench] decode sweep T={T}: {ms:.3f} ms, {n_active} experts", file=sys.stderr,
+              flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +184,8 @@ def main():
                     choices=["tiny", "decode", "prefill", "skewed", "stack"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-sweep", action="store_true",
+                    help="skip the T = 1..16 small-batch lines of the decode workload")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="oracle sample size (default sized to ~10-30 s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -248,7 +287,9 @@ def main():
         roofline["traffic"] = measured_traffic(w.name)
         per_expert = (w.T * w.k) // w.E
         if per_expert <= 32:
-            kname = "skinny_gemm_kernel<SWIGLU>"
+            kname = ("stream_gemm_kernel<SWIGLU>"
+                     if w.dtype == "bf16" and min(w.d, w.d_ff) >= 352 else
+                     "skinny_gemm_kernel<SWIGLU>")
         elif per_expert <= 256 or w.dtype == "f32":
             kname = "grouped_gemm_kernel<SWIGLU>"
         else:
@@ -269,6 +310,10 @@ def main():
                                 (PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS), 4),
              "active_experts": n_active}
 
+    sweep = None
+    if w.name == "decode" and not args.no_decode_sweep:
+        sweep = decode_sweep(w, L, moe, np, torch, stream, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline and blocks is None:
         budget = args.cpu_tokens or max(8, min(w.T, 48))
@@ -285,6 +330,8 @@ def main():
                    "seed": args.seed},
         "roofline": roofline, "cpu_baseline": cpu, "layer_roofline": layer,
     }
+    if sweep is not None:
+        out["decode_sweep"] = sweep
     print(json.dumps(out), flush=True)
 
 

@@ -372,6 +372,52 @@ def test_full_size_layer(name):
     _forward_and_check(w, L, rows=rows)
 
 
+# ------------------------------------------------------ decode sweep T = 1..16
+
+@pytest.fixture(scope="module")
+def decode16():
+    """The decode workload's layer at T = 16; smaller batches take its first
+    T token rows (the weights do not depend on T)."""
+    w = WORKLOADS["decode"].with_(name="decode-sweep", T=16)
+    return w, _case(w)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16])
+def test_decode_sweep(decode16, T):
+    """Mixtral-shaped decode batches of 1..16 tokens: each token takes exactly
+    two experts, so T tokens touch at most min(8, 2T) of them (expected
+    8 (1 - 0.75^T) for independent uniform choices); empty experts must be
+    skipped, and every token must match the oracle."""
+    w0, L0 = decode16
+    w = w0.with_(name=f"decode-T{T}", T=T)
+    L = dict(L0, x=L0["x"][:T].contiguous())
+    y, ref = _forward_and_check(w, L)
+    counts = np.bincount(ref["idx"].ravel(), minlength=w.E)
+    log(f"  T={T}: {int((counts > 0).sum())} experts active, counts {counts.tolist()}")
+    assert (counts > 0).sum() <= min(w.E, 2 * T)
+
+
+def test_decode_single_token_reads_only_its_two_experts(decode16):
+    """T = 1: NaN in the six experts the token does not choose must leave y
+    bit for bit unchanged (their weights are never read)."""
+    w0, L0 = decode16
+    w = w0.with_(name="decode-T1", T=1)
+    x = L0["x"][:1].contiguous()
+    y = moe.moe_forward(x, L0["Wg"], L0["W1"], L0["W3"], L0["W2"], w.k)
+    idx, _ = moe.moe_route(x, L0["Wg"], w.k)
+    torch.cuda.synchronize()
+    chosen = set(to_np(idx).ravel().tolist())
+    assert len(chosen) == 2
+    P = {n: L0[n].clone() for n in ("W1", "W3", "W2")}
+    for e in range(w.E):
+        if e not in chosen:
+            for n in P:
+                P[n][e] = float("nan")
+    y_nan = moe.moe_forward(x, L0["Wg"], P["W1"], P["W3"], P["W2"], w.k)
+    torch.cuda.synchronize()
+    assert torch.equal(y_nan, y)
+
+
 @pytest.mark.timeout(900)
 def test_full_size_stack():
     from sparse_mixture_experts_31_amd.inputs import make_stack
