@@ -45,6 +45,7 @@ def lib():
         L.orc_router_logits.argtypes = [P, i32, P, i64, i32, i32, P, i32]
         L.orc_topk_gates.argtypes = [P, i64, i32, i32, P, P, P, P]
         L.orc_permute.argtypes = [P, i64, i32, i32, P, P, P, P]
+        L.orc_balance.argtypes = [P, P, i64, i32, i32, P, P, P]
         L.orc_swiglu_expert.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P]
         L.orc_moe_rows.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32, i32, P, i64,
                                    P, P, P, P, P, i32]
@@ -131,6 +132,21 @@ def route(x, Wg, k, nthreads=None):
     lg = router_logits(x, Wg, nthreads)
     idx, gates, go, gs = topk_gates(lg, k)
     return dict(logits=lg, idx=idx, gates=gates, gap_order=go, gap_set=gs)
+
+
+def balance(logits, idx):
+    """Router load statistics: f[e] (share of the T*k assignments), P[e]
+    (mean full-softmax probability) and laux = E * sum f * P."""
+    lg = np.ascontiguousarray(logits, np.float64)
+    ia = np.ascontiguousarray(idx, np.int32)
+    T, E = lg.shape
+    k = ia.shape[1]
+    f = np.empty(E, np.float64)
+    P = np.empty(E, np.float64)
+    laux = np.empty(1, np.float64)
+    _check(lib().orc_balance(_ptr(lg), _ptr(ia), T, E, k, _ptr(f), _ptr(P), _ptr(laux)),
+           "balance")
+    return dict(f=f, P=P, laux=float(laux[0]))
 
 
 def permute(idx, E):

@@ -184,6 +184,44 @@ int orc_topk_gates(const double *logits, long T, int E, int k, int32_t *idx,
     return 0;
 }
 
+/* ---- load statistics ---------------------------------------------------- */
+
+/* The loss the pages add in training is smallest when both the routed tokens
+ * and the router's probabilities spread evenly over the experts
+ * [tokentrails lineage, step "Load balancing"].  f is the share of routed
+ * assignments per expert, P the mean over tokens of the full softmax over
+ * the E scores; the loss multiplies their dot product by the expert count. */
+int orc_balance(const double *logits, const int32_t *idx, long T, int E, int k, double *f,
+                double *P, double *laux) {
+    if (T < 1 || E < 1 || E > 64 || k < 1 || k > E || !logits || !idx || !f || !P || !laux)
+        return -1;
+    for (int e = 0; e < E; ++e) {
+        f[e] = 0.0;
+        P[e] = 0.0;
+    }
+    for (long a = 0; a < T * (long)k; ++a) {
+        if (idx[a] < 0 || idx[a] >= E) return -1;
+        f[idx[a]] += 1.0;
+    }
+    for (int e = 0; e < E; ++e) f[e] /= (double)(T * (long)k);
+    for (long t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        double m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m) m = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) z += exp(l[e] - m);
+        for (int e = 0; e < E; ++e) P[e] += exp(l[e] - m) / z;
+    }
+    double s = 0.0;
+    for (int e = 0; e < E; ++e) {
+        P[e] /= (double)T;
+        s += f[e] * P[e];
+    }
+    *laux = (double)E * s;
+    return 0;
+}
+
 /* ---- grouping assignments by expert ------------------------------------ */
 
 /* Each expert receives the rows routed to it and some receive none

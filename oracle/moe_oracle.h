@@ -53,6 +53,17 @@ int orc_router_logits(const void *x, int x_dt, const float *Wg, long T, int d, i
 int orc_topk_gates(const double *logits, long T, int E, int k, int32_t *idx,
                    double *gates, double *gap_order, double *gap_set);
 
+/* Router load statistics and the load-balancing loss
+ * [tokentrails lineage, step "Load balancing" and the Code listing's last
+ * line: Laux = N * sum_i f_i * P_i, N the number of experts]:
+ *   f[e] = share of the T*k assignments routed to expert e (sums to 1),
+ *   P[e] = the router's softmax probability of expert e over all E scores,
+ *          averaged over the T tokens (sums to 1),
+ *   laux = E * sum_e f[e] * P[e].
+ * logits [T][E] fp64, idx [T][k] the choices; T >= 1. */
+int orc_balance(const double *logits, const int32_t *idx, long T, int E, int k, double *f,
+                double *P, double *laux);
+
 /* Stable counting sort of the T*k assignments by expert.  Assignment (t,j)
  * gets a row in expert idx[t][j]'s contiguous block; inside a block rows go in
  * ascending t, then j.  counts[E], offsets[E+1] (exclusive scan),

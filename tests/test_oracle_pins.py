@@ -420,3 +420,70 @@ def test_skewed_generator_half_the_load_on_two_experts():
     assert np.all(np.diff(counts) <= counts.max() * 0.1 + 0)  # roughly Zipf-ordered
     first, overlap = _consecutive_stats(idx)
     assert first > 0.5 and overlap > 0.9    # AR(1) tokens share experts
+
+
+# ------------------------------------------------------- load-balancing loss
+
+
+def _balance_of(x, Wg, k):
+    r = oracle.route(x, Wg, k)
+    return r, oracle.balance(r["logits"], r["idx"])
+
+
+def test_balance_uniform_router_gives_one():
+    """Wg = 0: every score is 0, so P is uniform (1/E each) and ties send
+    every token to experts 0..k-1 (f = 1/k there).  Laux = E * k * (1/k)(1/E)
+    = 1, whatever E and k."""
+    for E, k in ((8, 2), (13, 3), (4, 1)):
+        x = torch.randn(37, 64, generator=torch.Generator().manual_seed(E))
+        r, b = _balance_of(x, torch.zeros(E, 64), k)
+        np.testing.assert_allclose(b["P"], np.full(E, 1.0 / E), rtol=0, atol=1e-15)
+        want_f = np.zeros(E)
+        want_f[:k] = 1.0 / k
+        np.testing.assert_array_equal(b["f"], want_f)
+        assert abs(b["laux"] - 1.0) < 1e-14
+
+
+def test_balance_collapsed_router_gives_E():
+    """Every token scores expert 0 far above the rest (k = 1): all routed
+    assignments and all probability sit on expert 0, Laux = E * 1 * 1 = E,
+    the largest value the loss can take."""
+    E, d = 8, 32
+    x = torch.ones(50, d)
+    Wg = torch.zeros(E, d)
+    Wg[0, 0] = 1000.0
+    r, b = _balance_of(x, Wg, 1)
+    assert (r["idx"] == 0).all()
+    assert b["f"][0] == 1.0 and b["P"][0] == 1.0
+    assert b["laux"] == float(E)
+
+
+def test_balance_one_token_per_expert_gives_one():
+    """T = E tokens, token t scoring expert t high and all others equal
+    (k = 1): f = 1/E, and P_i = (p_self + (E-1) p_other) / E = 1/E by
+    symmetry, so Laux = E * E * (1/E)(1/E) = 1 even though no single
+    token's probabilities are uniform."""
+    E, d = 8, 16
+    x = torch.eye(E, d)
+    Wg = 6.0 * torch.eye(E, d)
+    r, b = _balance_of(x, Wg, 1)
+    np.testing.assert_array_equal(r["idx"][:, 0], np.arange(E))
+    np.testing.assert_allclose(b["f"], 1.0 / E, rtol=0, atol=0)
+    np.testing.assert_allclose(b["P"], 1.0 / E, rtol=0, atol=1e-15)
+    assert abs(b["laux"] - 1.0) < 1e-14
+
+
+def test_balance_relabelling_experts_permutes_f_and_P():
+    """Relabelling the experts (permuting the rows of Wg) permutes f and P the
+    same way and leaves Laux unchanged; both always sum to one."""
+    w, L = _tiny(3)
+    perm = np.random.default_rng(4).permutation(w.E)
+    r1, b1 = _balance_of(L["x"], L["Wg"], w.k)
+    r2, b2 = _balance_of(L["x"], L["Wg"][torch.from_numpy(perm)], w.k)
+    np.testing.assert_allclose(b2["f"], b1["f"][perm], rtol=0, atol=0)
+    np.testing.assert_allclose(b2["P"], b1["P"][perm], rtol=1e-14, atol=1e-17)
+    assert abs(b1["laux"] - b2["laux"]) < 1e-13
+    assert abs(b1["f"].sum() - 1.0) < 1e-15 and abs(b1["P"].sum() - 1.0) < 1e-14
+    # the pages' reading that the loss is lowest when spread evenly: a
+    # routing that is far from even scores above the uniform one
+    assert b1["laux"] > 1.0 - 1e-12
