@@ -86,6 +86,26 @@ moe_status moe_route(const void *x, const float *Wg, moe_dtype dt, int64_t T, in
                      int k, int32_t *topk_idx, float *topk_w, float *logits_or_null,
                      void *stream);
 
+/* Router plus its load statistics, for training's load-balancing loss:
+ * the same topk_idx / topk_w as moe_route, and
+ *   -> f_out fp32 [E]: share of the T*k routed assignments that went to
+ *      expert e (sums to 1),
+ *   -> P_out fp32 [E]: the router's softmax probability of expert e over all
+ *      E scores, averaged over the T tokens (sums to 1),
+ *   -> laux_out fp32 [1]: E * sum_e f_out[e] * P_out[e] (1 when routing and
+ *      probabilities are spread evenly, E when all go to one expert).
+ * Statistics are summed in fp64 in a fixed order (deterministic) and rounded
+ * once to fp32.  T >= 1.  ws: at least moe_route_balance_workspace_size(T, E)
+ * bytes (256-byte aligned).
+ * Defined by: tokentrails lineage, step "Load balancing" (Laux = N sum f_i
+ * P_i) and the Code listing's last line (share routed times mean
+ * probability, times the number of experts). */
+size_t moe_route_balance_workspace_size(int64_t T, int E);
+moe_status moe_route_balance(const void *x, const float *Wg, moe_dtype dt, int64_t T, int d,
+                             int E, int k, int32_t *topk_idx, float *topk_w, float *f_out,
+                             float *P_out, float *laux_out, void *ws, size_t ws_bytes,
+                             void *stream);
+
 /* Dispatch: group the T*k (token, slot) assignments by expert.
  *   topk_idx int32 [T][k] with entries in [0, E)
  *   -> counts int32 [E]; offsets int32 [E+1] = exclusive scan of counts

@@ -142,6 +142,39 @@ moe_status moe_route(const void *x, const float *Wg, moe_dtype dt, int64_t T, in
     return ok();
 }
 
+size_t moe_route_balance_workspace_size(int64_t T, int E) {
+    if (T < 1 || E < 1 || E > 64) return 0;
+    const size_t blocks = (size_t)moe_router_blocks(T);
+    return up(blocks * E * sizeof(double)) + up(blocks * E * sizeof(int32_t));
+}
+
+moe_status moe_route_balance(const void *x, const float *Wg, moe_dtype dt, int64_t T, int d,
+                             int E, int k, int32_t *topk_idx, float *topk_w, float *f_out,
+                             float *P_out, float *laux_out, void *ws, size_t ws_bytes,
+                             void *stream) {
+    CHECK(check_shape(T, d, 64, E, k, dt, false));
+    if (T < 1) return fail(MOE_ERR_INVALID_ARG, "load statistics need T >= 1 (T = %lld)",
+                           (long long)T);
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(Wg, 16);
+    REQUIRE_PTR(topk_idx, 4);
+    REQUIRE_PTR(topk_w, 4);
+    REQUIRE_PTR(f_out, 4);
+    REQUIRE_PTR(P_out, 4);
+    REQUIRE_PTR(laux_out, 4);
+    const size_t need = moe_route_balance_workspace_size(T, E);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+    REQUIRE_PTR(ws, kAlign);
+    const size_t blocks = (size_t)moe_router_blocks(T);
+    double *part_p = (double *)ws;
+    int32_t *part_c = at<int32_t>(ws, up(blocks * E * sizeof(double)));
+    LAUNCH(moe_launch_route_balance(x, (int)dt, Wg, T, d, E, k, topk_idx, topk_w, part_p, part_c,
+                                    f_out, P_out, laux_out, (hipStream_t)stream),
+           "route_balance");
+    return ok();
+}
+
 moe_status moe_permute(const void *x, const int32_t *topk_idx, moe_dtype dt, int64_t T, int d,
                        int E, int k, int32_t *counts, int32_t *offsets, int32_t *row_of,
                        int32_t *token_of, void *x_perm, void *ws, size_t ws_bytes,

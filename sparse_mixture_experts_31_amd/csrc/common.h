@@ -61,6 +61,14 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double v) {
 
 hipError_t moe_launch_router(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
                              int k, int32_t *idx, float *gw, float *logits, hipStream_t s);
+// Workgroups of the router launch for T tokens (one statistics row each).
+int64_t moe_router_blocks(int64_t T);
+// Router plus load statistics: part_p [blocks][E] fp64 and part_c [blocks][E]
+// int32 scratch; f, P [E] and laux [1] out (fp32).
+hipError_t moe_launch_route_balance(const void *x, int dt, const float *Wg, int64_t T, int d,
+                                    int E, int k, int32_t *idx, float *gw, double *part_p,
+                                    int32_t *part_c, float *f, float *P, float *laux,
+                                    hipStream_t s);
 hipError_t moe_launch_dispatch_index(const int32_t *idx, int64_t A, int E, int k,
                                      int32_t *counts, int32_t *offsets, int32_t *row_of,
                                      int32_t *token_of, hipStream_t s);

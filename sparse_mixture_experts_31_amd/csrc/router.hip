@@ -68,13 +68,20 @@ constexpr int kRouterWaves = 4;
 
 // WPT waves share each group of TPW tokens, every wave covering a contiguous
 // 1/WPT of d; their fp64 partial sums meet in LDS and are added in wave order.
-template <typename Tin, int TPW, int EG, int WPT>
+// With STATS the workgroup also leaves, for the load-balancing statistics,
+// the sum over its tokens (in token order) of each expert's full softmax
+// probability (fp64, part_p[block][E]) and how many of its tokens' choices
+// went to each expert (part_c[block][E]).
+template <typename Tin, int TPW, int EG, int WPT, bool STATS = false>
 __global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
     const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,
-    int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits) {
+    int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits,
+    double *__restrict__ part_p = nullptr, int32_t *__restrict__ part_c = nullptr) {
     constexpr int kGroups = kRouterWaves / WPT;  // token groups per workgroup
     __shared__ float s_logit[kGroups][TPW][64];
     __shared__ double s_part[kGroups][WPT][TPW * EG];
+    __shared__ double s_prob[STATS ? kGroups * TPW : 1][64];
+    __shared__ int s_sel[STATS ? kGroups * TPW : 1][8];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int grp = wave / WPT, part = wave % WPT;
@@ -124,81 +131,188 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
         __syncthreads();
     }
 
-    if (part != 0) return;
-    // scores out (optional), coalesced over the group's TPW x E block
-    if (out_logits) {
-        for (int q = lane; q < TPW * E; q += kWave) {
-            const int t = q / E, e = q % E;
-            if (tok0 + t < T) out_logits[(tok0 + t) * E + e] = s_logit[grp][t][e];
+    if (part == 0) {
+        // scores out (optional), coalesced over the group's TPW x E block
+        if (out_logits) {
+            for (int q = lane; q < TPW * E; q += kWave) {
+                const int t = q / E, e = q % E;
+                if (tok0 + t < T) out_logits[(tok0 + t) * E + e] = s_logit[grp][t][e];
+            }
         }
-    }
-    if (lane < TPW && tok0 + lane < T) {
-        const int t = lane;
-        const float *L = s_logit[grp][t];
-        uint64_t used = 0;
-        int sel[8];
-        float sl[8];
+        if (lane < TPW) {
+            const int t = lane;
+            const bool valid = tok0 + t < T;
+            const float *L = s_logit[grp][t];
+            uint64_t used = 0;
+            int sel[8];
+            float sl[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            sel[j] = 0;
-            sl[j] = 0.f;
-            if (j < k) {
-                int best = -1;
-                float bv = 0.f;
-                for (int e = 0; e < E; ++e) {
-                    if ((used >> e) & 1ull) continue;
-                    const float v = L[e];
-                    if (best < 0 || v > bv) {
-                        best = e;
-                        bv = v;
+            for (int j = 0; j < 8; ++j) {
+                sel[j] = 0;
+                sl[j] = 0.f;
+                if (j < k) {
+                    int best = -1;
+                    float bv = 0.f;
+                    for (int e = 0; e < E; ++e) {
+                        if ((used >> e) & 1ull) continue;
+                        const float v = L[e];
+                        if (best < 0 || v > bv) {
+                            best = e;
+                            bv = v;
+                        }
+                    }
+                    used |= 1ull << best;
+                    sel[j] = best;
+                    sl[j] = bv;
+                }
+            }
+            if (valid) {
+                float z = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (j < k) z += expf(sl[j] - sl[0]);
+                const int64_t o = (tok0 + t) * k;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (j < k) {
+                        out_idx[o + j] = sel[j];
+                        out_w[o + j] = expf(sl[j] - sl[0]) / z;
                     }
                 }
-                used |= 1ull << best;
-                sel[j] = best;
-                sl[j] = bv;
+            }
+            if constexpr (STATS) {
+                // full softmax over all E scores (l_max = sl[0]), in fp64
+                const int slot = grp * TPW + t;
+                double zz = 0.0;
+                for (int e = 0; e < E; ++e) zz += exp((double)L[e] - (double)sl[0]);
+                for (int e = 0; e < E; ++e)
+                    s_prob[slot][e] = valid ? exp((double)L[e] - (double)sl[0]) / zz : 0.0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s_sel[slot][j] = (valid && j < k) ? sel[j] : -1;
             }
         }
-        float z = 0.f;
+    }
+    if constexpr (STATS) {
+        __syncthreads();
+        const int e = threadIdx.x;
+        if (e < E) {
+            double p = 0.0;
+            int c = 0;
+            for (int slot = 0; slot < kGroups * TPW; ++slot) {
+                p += s_prob[slot][e];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < k) z += expf(sl[j] - sl[0]);
-        const int64_t o = (tok0 + t) * k;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j < k) {
-                out_idx[o + j] = sel[j];
-                out_w[o + j] = expf(sl[j] - sl[0]) / z;
+                for (int j = 0; j < 8; ++j) c += (s_sel[slot][j] == e);
             }
+            part_p[(int64_t)blockIdx.x * E + e] = p;
+            part_c[(int64_t)blockIdx.x * E + e] = c;
         }
+    }
+}
+
+// The router's per-block statistics summed in a fixed order (16 contiguous
+// chunks of blocks per expert, then the chunks in order), so the result is
+// the same bit for bit on every run:
+//   f[e] = count_e / (T k), P[e] = (sum of the token probabilities) / T,
+//   laux = E * sum_e f[e] P[e]   (tokentrails lineage, step "Load balancing").
+__global__ __launch_bounds__(1024) void balance_reduce_kernel(
+    const double *__restrict__ part_p, const int32_t *__restrict__ part_c, int nblocks, int64_t T,
+    int E, int k, float *__restrict__ f_out, float *__restrict__ P_out,
+    float *__restrict__ laux_out) {
+    constexpr int kChunks = 16;
+    __shared__ double s_p[kChunks][64];
+    __shared__ long long s_c[kChunks][64];
+    __shared__ double s_fp[64];
+    const int e = threadIdx.x % 64, ch = threadIdx.x / 64;
+    if (e < E) {
+        const int b0 = (int)((int64_t)nblocks * ch / kChunks);
+        const int b1 = (int)((int64_t)nblocks * (ch + 1) / kChunks);
+        double p = 0.0;
+        long long c = 0;
+        for (int b = b0; b < b1; ++b) {
+            p += part_p[(int64_t)b * E + e];
+            c += part_c[(int64_t)b * E + e];
+        }
+        s_p[ch][e] = p;
+        s_c[ch][e] = c;
+    }
+    __syncthreads();
+    if (threadIdx.x < E) {
+        double p = 0.0;
+        long long c = 0;
+        for (int q = 0; q < kChunks; ++q) {
+            p += s_p[q][e];
+            c += s_c[q][e];
+        }
+        const double fe = (double)c / ((double)T * k), pe = p / (double)T;
+        f_out[e] = (float)fe;
+        P_out[e] = (float)pe;
+        s_fp[e] = fe * pe;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+        for (int q = 0; q < E; ++q) s += s_fp[q];
+        *laux_out = (float)((double)E * s);
     }
 }
 
 }  // namespace moe
 
-hipError_t moe_launch_router(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
-                             int k, int32_t *idx, float *gw, float *logits, hipStream_t s) {
+namespace {
+
+// Few tokens: four waves split each token's row, so a small batch still
+// spreads over many waves.  Many tokens: one wave per token, four tokens per
+// workgroup (measured on MI355X: 29 us against 46 us for four tokens per
+// wave at T = 4096; 7.7 us against 16.7 us the other way at T = 32).
+bool router_wide_rows(int64_t T) { return T < 1024; }
+
+template <bool STATS>
+hipError_t launch_router_impl(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
+                              int k, int32_t *idx, float *gw, float *logits, double *part_p,
+                              int32_t *part_c, hipStream_t s) {
     using namespace moe;
     const dim3 block(kRouterWaves * kWave);
-    // Few tokens: four waves split each token's row, so a small batch still
-    // spreads over many waves.  Many tokens: one wave per token, four tokens
-    // per workgroup (measured on MI355X: 29 us against 46 us for four tokens
-    // per wave at T = 4096; 7.7 us against 16.7 us the other way at T = 32).
-    if (T < 1024) {
-        const dim3 grid((unsigned)T);
+    const dim3 grid((unsigned)moe_router_blocks(T));
+    if (router_wide_rows(T)) {
         if (dt == 0)
-            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 4>), grid, block, 0, s,
-                               (const float *)x, Wg, T, d, E, k, idx, gw, logits);
+            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 4, STATS>), grid, block, 0, s,
+                               (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p, part_c);
         else
-            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 4>), grid, block, 0, s,
-                               (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits);
+            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 4, STATS>), grid, block, 0, s,
+                               (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, part_p,
+                               part_c);
     } else {
-        const dim3 grid((unsigned)((T + kRouterWaves - 1) / kRouterWaves));
         if (dt == 0)
-            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 1>), grid, block, 0, s,
-                               (const float *)x, Wg, T, d, E, k, idx, gw, logits);
+            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 1, STATS>), grid, block, 0, s,
+                               (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p, part_c);
         else
-            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 1>), grid, block, 0, s,
-                               (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits);
+            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 1, STATS>), grid, block, 0, s,
+                               (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, part_p,
+                               part_c);
     }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t moe_router_blocks(int64_t T) {
+    return router_wide_rows(T) ? T : (T + moe::kRouterWaves - 1) / moe::kRouterWaves;
+}
+
+hipError_t moe_launch_router(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
+                             int k, int32_t *idx, float *gw, float *logits, hipStream_t s) {
+    return launch_router_impl<false>(x, dt, Wg, T, d, E, k, idx, gw, logits, nullptr, nullptr,
+                                     s);
+}
+
+hipError_t moe_launch_route_balance(const void *x, int dt, const float *Wg, int64_t T, int d,
+                                    int E, int k, int32_t *idx, float *gw, double *part_p,
+                                    int32_t *part_c, float *f, float *P, float *laux,
+                                    hipStream_t s) {
+    hipError_t err = launch_router_impl<true>(x, dt, Wg, T, d, E, k, idx, gw, nullptr, part_p,
+                                              part_c, s);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(moe::balance_reduce_kernel, dim3(1), dim3(1024), 0, s, part_p, part_c,
+                       (int)moe_router_blocks(T), T, E, k, f, P, laux);
     return hipGetLastError();
 }

@@ -45,8 +45,11 @@ def lib():
         L.moe_last_error.argtypes = []
         L.moe_workspace_size.restype = sz
         L.moe_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+        L.moe_route_balance_workspace_size.restype = sz
+        L.moe_route_balance_workspace_size.argtypes = [i64, i32]
         sigs = {
             "moe_route": [P, P, i32, i64, i32, i32, i32, P, P, P, P],
+            "moe_route_balance": [P, P, i32, i64, i32, i32, i32, P, P, P, P, P, P, sz, P],
             "moe_permute": [P, P, i32, i64, i32, i32, i32, P, P, P, P, P, P, sz, P],
             "moe_expert_ffn": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, sz, P],
             "moe_combine": [P, P, P, P, i32, i64, i32, i32, P, P],
@@ -119,6 +122,32 @@ def moe_route(x, Wg, k, topk_idx=None, topk_w=None, logits=None, stream=None):
     _call("moe_route", _p(x), _p(Wg), _dt(x), T, d, E, k, _p(topk_idx), _p(topk_w), _p(logits),
           _s(stream))
     return topk_idx, topk_w
+
+
+def moe_route_balance_workspace_size(T, E) -> int:
+    return int(lib().moe_route_balance_workspace_size(T, E))
+
+
+def moe_route_balance(x, Wg, k, topk_idx=None, topk_w=None, ws=None, stream=None):
+    """moe_route plus the load statistics: returns (topk_idx, topk_w, f, P,
+    laux) with f, P fp32 [E] and laux an fp32 tensor of one element."""
+    T, d = x.shape
+    E = Wg.shape[0]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    f = torch.empty(E, dtype=torch.float32, device=x.device)
+    P = torch.empty(E, dtype=torch.float32, device=x.device)
+    laux = torch.empty(1, dtype=torch.float32, device=x.device)
+    if ws is None:
+        n = moe_route_balance_workspace_size(T, E)
+        if n == 0:
+            raise ValueError("shape rejected by libmoe")
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _call("moe_route_balance", _p(x), _p(Wg), _dt(x), T, d, E, k, _p(topk_idx), _p(topk_w),
+          _p(f), _p(P), _p(laux), _p(ws), ws.numel(), _s(stream))
+    return topk_idx, topk_w, f, P, laux
 
 
 def moe_permute(x, topk_idx, E, counts=None, offsets=None, row_of=None, token_of=None,

@@ -107,3 +107,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         moe.lib()
+
+
+def test_route_balance_workspace_size_rules():
+    ws = moe.moe_route_balance_workspace_size
+    assert ws(0, 8) == 0 and ws(16, 65) == 0 and ws(16, 0) == 0
+    # one fp64 and one int32 statistics row per router workgroup
+    assert ws(32, 8) >= 32 * 8 * 12
+    assert ws(16384, 8) >= 4096 * 8 * 12
+    assert ws(16384, 8) > ws(4096, 8) > 0

@@ -427,3 +427,40 @@ def test_full_size_stack():
     sample = np.array([0, 1, 100, 333, 517, 777, 901, 1024, 1300, 1500, 1650, 1800, 1901, 2000,
                        2046, 2047])
     _stack_check(w, blocks, h0, sample)
+
+
+# ------------------------------------------------ load statistics of the router
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed"])
+def test_route_balance_matches_oracle(name):
+    """f (share routed per expert), P (mean full-softmax probability) and
+    Laux = E sum f P against the oracle; the routing outputs are those of
+    moe_route bit for bit, and two runs give the same bits."""
+    w = WORKLOADS[name]
+    L = _case(w)
+    idx, gw, f, P, laux = moe.moe_route_balance(L["x"], L["Wg"], w.k)
+    idx0, gw0 = moe.moe_route(L["x"], L["Wg"], w.k)
+    _, _, f2, P2, laux2 = moe.moe_route_balance(L["x"], L["Wg"], w.k)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx0) and torch.equal(gw, gw0)
+    assert torch.equal(f, f2) and torch.equal(P, P2) and torch.equal(laux, laux2)
+    ref = oracle.route(L["x"], L["Wg"], w.k)
+    check_routing(to_np(idx), to_np(gw), ref)
+    # f from the GPU's own choices is exact (an integer count over T*k)
+    counts = np.bincount(to_np(idx).ravel(), minlength=w.E)
+    np.testing.assert_array_equal(to_np(f), (counts / (w.T * w.k)).astype(np.float32))
+    b = oracle.balance(ref["logits"], ref["idx"])
+    # near-tie tokens may route differently: f then differs by those tokens
+    n_diff = int((to_np(idx) != ref["idx"]).any(1).sum())
+    assert np.abs(to_np(f).astype(np.float64) - b["f"]).max() <= (n_diff + 0.5) / (w.T * w.k)
+    # P from fp32-rounded scores, summed in fp64 and rounded once to fp32
+    np.testing.assert_allclose(to_np(P), b["P"], rtol=2e-6, atol=1e-8)
+    assert abs(float(laux[0]) - b["laux"]) <= 2e-6 * b["laux"] + 2.0 * n_diff / (w.T * w.k)
+    log(f"  Laux {float(laux[0]):.6f} (oracle {b['laux']:.6f}), f {np.round(to_np(f), 4).tolist()}")
+
+
+def test_route_balance_rejects_empty_batch():
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    Wg = torch.zeros((8, 128), dtype=torch.float32, device=DEV)
+    with pytest.raises(moe.MoeError):
+        moe.moe_route_balance(x, Wg, 2, ws=torch.empty(256, dtype=torch.uint8, device=DEV))
