@@ -5,6 +5,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -40,6 +41,15 @@ __device__ __forceinline__ f32x16 mma_step<float>(i32x4 a, i32x4 b, f32x16 c) {
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.z), __int_as_float(b.z), c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a.w), __int_as_float(b.w), c, 0, 0, 0);
     return c;
+}
+
+// acc += A_frag * B_frag over 32 bf16 k: 16 rows x 16 cols.  Lane l holds
+// row l % 16 (A) or column l % 16 (B) at k 8 (l / 16) .. + 8, and D rows
+// 4 (l / 16) .. + 4 of column l % 16.  Under random data this form sustains
+// about a quarter more throughput on MI355X than the 32 x 32 x 16 one.
+__device__ __forceinline__ f32x4 mma16(i32x4 a, i32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 template <typename T>

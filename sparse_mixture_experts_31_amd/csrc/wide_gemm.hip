@@ -8,26 +8,24 @@
 // Tiles.  256 weight rows x 256 token rows; for GEMM1 the weight rows are
 // 128 rows of W1 and the same 128 rows of W3.  Four waves in a 2 x 2 grid,
 // each owning 128 x 128 outputs in 256 accumulator registers (one wave per
-// SIMD).  Per 16-wide k-step a wave reads four weight and four token
-// fragments and issues 16 v_mfma_f32_32x32x16_bf16: half the LDS reads per
-// MFMA of the 8-wave tiles, whose 64 x 128 wave tiles keep the LDS port as
-// busy as the matrix cores.
+// SIMD) as 8 x 8 fragments of v_mfma_f32_16x16x32_bf16, the MFMA form that
+// sustains the most throughput on random data.  Per 32-wide k-step a wave
+// reads eight weight and eight token fragments and issues 64 MFMAs.
 //
-// k-loop.  The stage ring of expert_gemm.hip (global_load_lds straight into
-// swizzled LDS, explicit vmcnt waits, fence-free barrier) with three changes
-// that keep the single wave per SIMD issuing MFMAs:
-//  * fragment double buffering: the second k-half of a stage is read under
-//    the MFMAs of the first, the next stage's first half under the second
-//    half's, and the reads and loads are interleaved one by one with the
-//    MFMAs (scheduling groups), so no memory instruction waits at issue
-//    behind a full queue while the matrix core idles;
-//  * no branches: the slot a stage frees is refilled with the stage P ahead
-//    in this segment or the next (a select), and past the last segment with
-//    a reload of the same segment that nothing reads, so every stage issues
-//    the same loads and every vmcnt wait is a constant;
-//  * a ragged token tile runs all MFMAs (rows past the count hold a clamped
-//    valid row and are not stored): every wave meets every barrier, so
-//    skipping a dead wave's MFMAs would not shorten the tile.
+// k-loop.  A stage is 64 k: one whole 128-byte line of every weight and token
+// row, fetched by global_load_lds (eight lines per instruction) into a
+// swizzled two-slot LDS ring, with explicit vmcnt waits and a fence-free
+// barrier.  Fragments are double buffered: step 0 of a stage runs under the
+// reads of step 1, then one barrier frees the slot (its reads have landed),
+// and step 1 runs under the reads of the next stage's step 0 and the loads
+// that refill the slot two stages ahead, spread over the step so the
+// load path never backs up into the MFMA issue.  Scheduling groups fix the
+// interleaving; the loop has no branches (the slot a stage frees is refilled
+// with the stage two ahead in this segment or the next, and past the last
+// segment with a reload that nothing reads), so every vmcnt wait is a
+// constant.  A ragged token tile runs all MFMAs (rows past the count hold a
+// clamped valid row and are not stored): every wave meets every barrier, and
+// a second fragment count in the same kernel costs the full one registers.
 //
 // Schedule.  Workgroup b runs on XCD b % 8.  The tiles (token tiles fastest,
 // then weight tiles, then experts) are cut into eight contiguous ranges, one
@@ -47,15 +45,22 @@ namespace moe {
 namespace {
 
 constexpr int kWideBW = 256, kWideBT = 256, kWideWaves = 4;
-constexpr int kWideP = 4;  // stages in the ring
+constexpr int kWideP = 2;  // stages in the ring (double buffer)
 constexpr int kWideRows = kWideBW + kWideBT;
-constexpr int kWideLPW = kWideRows / 16 / kWideWaves;  // 16-row loads per wave per stage
-constexpr int kWideStageBytes = kWideRows * 64;
+constexpr int kWideLPW = kWideRows / 8 / kWideWaves;  // 8-row loads per wave per stage
+constexpr int kWideStageBytes = kWideRows * 128;
 constexpr int kWideLds = kWideP * kWideStageBytes;
-constexpr int kWideKStep = 32;                   // bf16 K elements per stage
+constexpr int kWideKStep = 64;                   // bf16 K elements per stage
 constexpr int kSlotFloats = kWideWaves * kWave * 256;  // accumulators of one workgroup
 static_assert(kWideLPW * (kWideP - 1) < 64, "vmcnt range");
 static_assert(kWideLds <= 160 * 1024 - 1024, "LDS capacity");
+
+// Byte offset of 16-byte chunk c of row r in a stage of 128-byte rows: the
+// chunk sits at c ^ ((r >> 1) & 7), so a 32-row operand read (16 lanes per
+// LDS cycle on 16 rows of one chunk) hits 16 distinct bank groups.
+__device__ __forceinline__ int swz128(int r, int c) {
+    return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
 
 // Per-expert tile table in LDS: first row, row count, first tile number.
 struct TileTable {
@@ -75,16 +80,21 @@ struct TileTable {
         }
         first[E] = f;
     }
-    __device__ int total() const { return first[E]; }
+    // The table is the same for every lane: reading it through
+    // readfirstlane keeps the tile and segment arithmetic in scalar
+    // registers, away from the vector registers the k-loop needs.
+    __device__ static int u(int v) { return __builtin_amdgcn_readfirstlane(v); }
+    __device__ int total() const { return u(first[E]); }
     __device__ TileInfo info(int t, int cols) const {
         int i = 0;
-        while (i + 1 < E && first[i + 1] <= t) ++i;
-        const int rem = t - first[i];
-        const int mtiles = (cnt[i] + kWideBT - 1) / kWideBT;
+        while (i + 1 < E && u(first[i + 1]) <= t) ++i;
+        const int rem = t - u(first[i]);
+        const int c = u(cnt[i]), l = u(lo[i]);
+        const int mtiles = (c + kWideBT - 1) / kWideBT;
         TileInfo ti;
         ti.e = i;
-        ti.row0 = lo[i] + (rem % mtiles) * kWideBT;
-        ti.mrem = min(kWideBT, lo[i] + cnt[i] - ti.row0);
+        ti.row0 = l + (rem % mtiles) * kWideBT;
+        ti.mrem = min(kWideBT, l + c - ti.row0);
         ti.n0 = (rem / mtiles) * cols;
         return ti;
     }
@@ -120,34 +130,37 @@ struct Segment {
     int tile, sb, se, slot;
 };
 
-// Store fragment (i, j) of a wave's 128 x 128 block: element q of a fragment
-// is D[n = 8 (q / 4) + 4 lhalf + q % 4][m = lrow].  GEMM1 passes the u
-// fragment and the matching v fragment and stores silu(u) * v.
+// Store fragment (i, j) of a wave's 128 x 128 block: lane l holds the
+// outputs of token row m = 32 j + 16 wm + l % 16 and weight rows
+// 16 i + 4 (l / 16) .. + 4.  GEMM1 passes the u fragment and the matching v
+// fragment and stores silu(u) * v.
 template <bool SWIGLU, typename TO>
 __device__ __forceinline__ void store_fragment(TO *__restrict__ out, int N, const TileInfo &ti,
                                                int wn, int wm, int lane, int i, int j,
-                                               const f32x16 &u, const f32x16 &v) {
-    const int lrow = lane & 31, lhalf = lane >> 5;
-    const int m = wm * 128 + j * 32 + lrow;
+                                               const f32x4 &u, const f32x4 &v) {
+    const int m = (2 * j + wm) * 16 + (lane & 15);
     if (m >= ti.mrem) return;
-    TO *orow = out + (int64_t)(ti.row0 + m) * N;
+    const int n = ti.n0 + (SWIGLU ? wn * 64 : wn * 128) + i * 16 + 4 * (lane >> 4);
+    if (n >= N) return;
+    float r[4];
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-        const int n = ti.n0 + (SWIGLU ? wn * 64 : wn * 128) + i * 32 + 8 * gq + 4 * lhalf;
-        if (n < N) {
-            float r[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                r[q] = u[4 * gq + q];
-                if constexpr (SWIGLU) r[q] = silu(r[q]) * v[4 * gq + q];
-            }
-            store4<TO>(orow + n, r[0], r[1], r[2], r[3]);
-        }
+    for (int q = 0; q < 4; ++q) {
+        r[q] = u[q];
+        if constexpr (SWIGLU) r[q] = silu(r[q]) * v[q];
     }
+    store4<TO>(out + (int64_t)(ti.row0 + m) * N + n, r[0], r[1], r[2], r[3]);
 }
 
-// Scratch slot layout: float4 number p (0..63) of thread t at 4 (p * 256 + t),
-// p = 4 (4 i + j) + gq, so every store and load of a wave is 1 KiB contiguous.
+// Says that every accumulator is in an accumulator register here.
+__device__ __forceinline__ void pin_accumulators(f32x4 (&acc)[8][8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+// Scratch slot layout: fragment p = 8 i + j (0..63) of thread t at float4
+// p * 256 + t, so every store and load of a wave is 1 KiB contiguous.
 __device__ __forceinline__ float *slot_ptr(float *partial, int slot) {
     return partial + (size_t)slot * kSlotFloats;
 }
@@ -205,15 +218,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         return sg;
     };
 
-    // Lane pointers of this wave's LPW 16-row loads of a tile: row r of a
-    // stage is loaded by wave (r / 16) % 4, lane 4 (r % 16) + chunk slot,
-    // fetching the chunk that belongs at that slot.  Loads [0, LPW / 2) are
-    // weight rows, the rest token rows (act rows, through `gather` if set).
+    // Lane pointers of this wave's LPW 8-row loads of a tile: row r of a
+    // stage is loaded by wave (r / 8) % 4, lane 8 (r % 8) + chunk slot,
+    // fetching the chunk that belongs at that slot; every load instruction
+    // moves eight whole 128-byte lines.  Loads [0, LPW / 2) are weight rows,
+    // the rest token rows (act rows, through `gather` if set).
     auto sources = [&](const TileInfo &ti, const char *(&src)[LPW]) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const int r = (wave + kWideWaves * i) * 16 + (lane >> 2);
-            const int c = (lane & 3) ^ ((r >> 2) & 3);
+            const int r = (wave + kWideWaves * i) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
             if (i < LPW / 2) {
                 const bf16_t *W = Wa;
                 int nr;
@@ -226,40 +240,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 nr = min(nr, N - 1);
                 src[i] = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + c * 16;
             } else {
-                const int row = act_row<16>(gather, ti.row0 + (wave + kWideWaves * i) * 16 - BW,
-                                            ti.row0 + ti.mrem - 1, lane);
+                const int row = act_row<8>(gather, ti.row0 + (wave + kWideWaves * i) * 8 - BW,
+                                           ti.row0 + ti.mrem - 1, lane);
                 src[i] = (const char *)(act + (int64_t)row * act_ld) + c * 16;
             }
         }
     };
 
     const int wn = wave & 1, wm = wave >> 1;
-    const int lrow = lane & 31, lhalf = lane >> 5;
-    // LDS row of weight fragment i (GEMM1: 0,1 are W1 rows, 2,3 the same W3 rows)
+    // LDS row of weight fragment i (GEMM1: 0..3 are W1 rows, 4..7 the same
+    // W3 rows)
     auto wrow = [&](int i) {
         if constexpr (SWIGLU)
-            return (i < 2 ? 0 : BW / 2) + wn * 64 + (i & 1) * 32;
+            return (i < 4 ? 0 : BW / 2) + wn * 64 + (i & 3) * 16;
         else
-            return wn * 128 + i * 32;
+            return wn * 128 + i * 16;
     };
-    const int trow0 = BW + wm * 128;
+    // LDS row of token fragment j: the two wave rows interleave 16-row
+    // fragments, so the first 32 j + 32 token rows sit in fragments <= j.
+    auto trow = [&](int j) { return BW + (2 * j + wm) * 16; };
+    // Lane part of a fragment read for k-step s of a stage: row l % 16 of the
+    // fragment, 16-byte chunk 4 s + l / 16 (fragment rows start at multiples
+    // of 16, so the swizzle depends on the lane only).
+    const int lr = lane & 15, lq = lane >> 4, lx = (lr >> 1) & 7;
+    const int roff[2] = {lr * 128 + ((lq ^ lx) << 4), lr * 128 + (((4 + lq) ^ lx) << 4)};
 
-    f32x16 acc[4][4];
-    i32x4 a0[4], b0[4], a1[4], b1[4];
-    auto load_frags = [&](i32x4 (&a)[4], i32x4 (&b)[4], int slot, int t) {
-        const char *base = smem + slot * kWideStageBytes;
-        const int c = 2 * t + lhalf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *(const i32x4 *)(base + lds_off(wrow(i) + lrow, c));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = *(const i32x4 *)(base + lds_off(trow0 + j * 32 + lrow, c));
+    f32x4 acc[8][8];
+    i32x4 a0[8], b0[8], a1[8], b1[8];
+    // Fragment read k of k-step s (k < 8: weight fragment k, else token
+    // fragment k - 8) from a slot.
+    auto read_frag = [&](i32x4 (&a)[8], i32x4 (&b)[8], int slot, int s, int k)
+        __attribute__((always_inline)) {
+        const char *base = smem + slot * kWideStageBytes + roff[s];
+        if (k < 8)
+            a[k] = *(const i32x4 *)(base + wrow(k) * 128);
+        else
+            b[k - 8] = *(const i32x4 *)(base + trow(k - 8) * 128);
     };
-    auto mma = [&](const i32x4 (&a)[4], const i32x4 (&b)[4]) {
+    // MFMAs [m0, m1) of a k-step, fragment (m / 8, m % 8) for MFMA m.
+    auto mma_part = [&](const i32x4 (&a)[8], const i32x4 (&b)[8], int m0, int m1)
+        __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mma_step<bf16_t>(a[i], b[j], acc[i][j]);
+        for (int m = m0; m < m1; ++m)
+            acc[m / 8][m % 8] = mma16(a[m / 8], b[m % 8], acc[m / 8][m % 8]);
     };
 
     // The producer runs P stages ahead of the consumer with its own cursor:
@@ -270,11 +293,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // reads, so every stage issues the same loads.
     const char *pp[LPW];
     int p_left;
-    auto produce_from = [&](int k) {
+    auto produce_from = [&](int k) __attribute__((always_inline)) {
         const Segment sg = segment(min(k, n_seg - 1));
         sources(tt.info(sg.tile, kCols), pp);
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) pp[i] += (int64_t)sg.sb * 64;
+        for (int i = 0; i < LPW; ++i) pp[i] += (int64_t)sg.sb * 128;
         p_left = (k < n_seg) ? sg.se - sg.sb : 0x7fffffff;
     };
     int p_seg = 0;
@@ -285,101 +308,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             dma16(pp[i], dst + (wave + kWideWaves * i) * 1024);
-            pp[i] += 64;
+            pp[i] += 128;
         }
     }
     p_left -= P;
     if (p_left == 0) produce_from(++p_seg);
     wait_vmcnt_lgkm0<LPW * (P - 1)>();
     stage_barrier();
-    load_frags(a0, b0, 0, 0);
 
     int g = 0;  // stages consumed so far = ring cursor
     for (int c_k = 0; c_k < n_seg; ++c_k) {
         const Segment cur = segment(c_k);
         const TileInfo ti = tt.info(cur.tile, kCols);
+        // Accumulators start at zero, and are held in the accumulator
+        // registers (said at the start and at the end of every stage, so
+        // the allocator never parks one in a vector register).
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-        // Only fragment reads are pending inside the k-loop; a clean count
-        // here lets the compiler's own waits stay exact.
+            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
+        pin_accumulators(acc);
+        // The k-loop of one segment.  Each step is cut into chunks by
+        // scheduling barriers, so every read and load issues between the
+        // MFMAs it is placed among.
+        // Step 0 of the segment's first stage (the previous segment read it
+        // too, but the ring may have moved on since).
+#pragma unroll
+        for (int k = 0; k < 16; ++k) read_frag(a0, b0, g % P, 0, k);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-
         for (int s = cur.sb; s < cur.se; ++s, ++g) {
             const int slot = g % P;
-            // Second k-half of this stage, under the MFMAs of the first.
+            // Step 0 under the reads of step 1, two MFMAs per read, so the
+            // last read still has 32 MFMAs to land under.
             __builtin_amdgcn_sched_barrier(0);
-            load_frags(a1, b1, slot, 1);
-            mma(a0, b0);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            for (int k = 0; k < 16; ++k) {
+                read_frag(a1, b1, slot, 1, k);
+                mma_part(a0, b0, 2 * k, 2 * k + 2);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            mma_part(a0, b0, 32, 64);
             __builtin_amdgcn_sched_barrier(0);
-            // Next stage landed (this wave's loads, then everyone's), and
-            // every wave is done reading this slot.
+            // Every read of this slot has landed and the next stage's loads
+            // too (this wave's, then everyone's): free the slot.
             wait_vmcnt_lgkm0<LPW * (P - 2)>();
             stage_barrier();
-            // Refill this slot P stages ahead; read the next stage's first
-            // k-half; both under the MFMAs of this stage's second half.
+            // Step 1 under the reads of the next stage's step 0 and the
+            // loads refilling this slot P stages ahead: one read and one
+            // load per three MFMAs, then 16 MFMAs for the last read to land.
+            static_assert(LPW == 16, "one load per fragment read");
             char *dst = smem + slot * kWideStageBytes;
-            load_frags(a0, b0, (g + 1) % P, 0);
 #pragma unroll
-            for (int i = 0; i < LPW; ++i) {
-                dma16(pp[i], dst + (wave + kWideWaves * i) * 1024);
-                pp[i] += 64;
+            for (int k = 0; k < 16; ++k) {
+                read_frag(a0, b0, (g + 1) % P, 0, k);
+                dma16(pp[k], dst + (wave + kWideWaves * k) * 1024);
+                pp[k] += 128;
+                mma_part(a1, b1, 3 * k, 3 * k + 3);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            mma(a1, b1);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global->LDS load
-            }
+            mma_part(a1, b1, 48, 64);
             __builtin_amdgcn_sched_barrier(0);
-            // The reads above were issued before eight MFMAs and have landed;
-            // saying so keeps the compiler's next wait at the next eight.
+            // The reads above have landed by now; saying so keeps the
+            // compiler's next wait exact.
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
             if (--p_left == 0) produce_from(++p_seg);  // the producer's next segment
+            pin_accumulators(acc);
         }
 
         if (cur.slot < 0) {
             // Epilogue.  Each fragment is pinned in accumulator registers up
-            // to its turn, so they are moved out one at a time and not all
+            // to its turn, so they are moved out a few at a time and not all
             // 256 at the loop exit.
-            constexpr int NI = SWIGLU ? 2 : 4;
+            constexpr int NI = SWIGLU ? 4 : 8;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 8; ++j) {
                     asm volatile("" : "+a"(acc[i][j]));
-                    if constexpr (SWIGLU) asm volatile("" : "+a"(acc[i + 2][j]));
+                    if constexpr (SWIGLU) asm volatile("" : "+a"(acc[i + 4][j]));
                     store_fragment<SWIGLU, TO>(out, N, ti, wn, wm, lane, i, j, acc[i][j],
-                                               acc[SWIGLU ? i + 2 : i][j]);
+                                               acc[SWIGLU ? i + 4 : i][j]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         } else {
             float *dst = slot_ptr(partial, blockIdx.x * 2 + cur.slot);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 8; ++i) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 8; ++j) {
                     asm volatile("" : "+a"(acc[i][j]));
-#pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        const int p = 4 * (4 * i + j) + gq;
-                        *(float4 *)(dst + 4 * (p * 256 + tid)) =
-                            make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1],
-                                        acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-                    }
+                    const int p = 8 * i + j;
+                    *(f32x4 *)(dst + 4 * (p * 256 + tid)) = acc[i][j];
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -389,9 +409,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // Sums the parts of every split tile in workgroup order and applies the
-// epilogue.  Block b handles fragment b % 16 (GEMM1: u/v pair b % 8; the
-// other eight blocks exit) of tile b / 128 of the split round of XCD
-// (b / 16) % 8: one fragment per block keeps many loads in flight.
+// epilogue.  Block b handles fragments 4 (b % 16) .. + 4 of every wave
+// (GEMM1: u fragments, with their v fragments 32 further; the other eight
+// blocks exit) of tile b / 128 of the split round of XCD (b / 16) % 8: a
+// few fragments per block keep many loads in flight.
 template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restrict__ offsets,
                                                          int E, int N, int K, int A, int G8,
@@ -431,28 +452,20 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
     const TileInfo ti = tt.info(s_tile, kCols);
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int wn = wave & 1, wm = wave >> 1;
-    auto load_sum = [&](int i, int j) {
-        f32x16 r{};
+    auto load_sum = [&](int p) {
+        f32x4 r{};
 #pragma unroll 4
-        for (int k = 0; k < np; ++k) {
-            const float *src = partial + (size_t)s_slots[k] * kSlotFloats;
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int p = 4 * (4 * i + j) + gq;
-                const float4 v = *(const float4 *)(src + 4 * (p * 256 + tid));
-                r[4 * gq] += v.x;
-                r[4 * gq + 1] += v.y;
-                r[4 * gq + 2] += v.z;
-                r[4 * gq + 3] += v.w;
-            }
-        }
+        for (int k = 0; k < np; ++k)
+            r += *(const f32x4 *)(partial + (size_t)s_slots[k] * kSlotFloats + 4 * (p * 256 + tid));
         return r;
     };
-    // GEMM1: u/v fragment pair (i, j), i < 2; GEMM2: fragment (i, j)
-    const int i = frag / 4, j = frag % 4;
-    const f32x16 u = load_sum(i, j);
-    const f32x16 v = SWIGLU ? load_sum(i + 2, j) : u;
-    store_fragment<SWIGLU, TO>(out, N, ti, wn, wm, lane, i, j, u, v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int p = 4 * frag + q;  // GEMM1: u fragment (p < 32); GEMM2: any fragment
+        const f32x4 u = load_sum(p);
+        const f32x4 v = SWIGLU ? load_sum(p + 32) : u;
+        store_fragment<SWIGLU, TO>(out, N, ti, wn, wm, lane, p / 8, p % 8, u, v);
+    }
 }
 
 namespace {

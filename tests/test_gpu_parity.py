@@ -57,6 +57,11 @@ SMALL = [
     # more wide tiles than workgroups (the load ring crosses tiles), the
     # shortest k-loop (d = 128) and a W2 tile half past N
     Workload("wide-many", 18, T=2048, d=128, d_ff=2304),
+    # every token takes both of two experts: 300 rows each, a full 256-row
+    # tile and a narrow one of 44 rows (the quarter-MFMA k-loop)
+    Workload("wide-narrow", 19, T=300, d=256, d_ff=512, E=2, k=2),
+    # ~300 rows per expert from a random split: narrow last tiles again
+    Workload("wide-narrow-k1", 22, T=600, d=192, d_ff=640, E=2, k=1),
 ]
 
 
