@@ -129,6 +129,7 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * 64 + ((c ^ ((r
 
 struct TileInfo {
     int e, row0, mrem, n0;
+    int mt;  // token tile index within its expert (wide_gemm.hip)
 };
 
 static inline int device_cus() {

@@ -49,7 +49,9 @@ constexpr int kWideP = 2;  // stages in the ring (double buffer)
 constexpr int kWideRows = kWideBW + kWideBT;
 constexpr int kWideLPW = kWideRows / 8 / kWideWaves;  // 8-row loads per wave per stage
 constexpr int kWideStageBytes = kWideRows * 128;
-constexpr int kWideLds = kWideP * kWideStageBytes;
+constexpr int kWidePfBytes = 256;  // where the L2 prefetches land (never read)
+constexpr int kWideLds = kWideP * kWideStageBytes + kWidePfBytes;
+constexpr int kWidePfAhead = 2;   // stages past the one being loaded
 constexpr int kWideKStep = 64;                   // bf16 K elements per stage
 constexpr int kSlotFloats = kWideWaves * kWave * 256;  // accumulators of one workgroup
 static_assert(kWideLPW * (kWideP - 1) < 64, "vmcnt range");
@@ -93,7 +95,8 @@ struct TileTable {
         const int mtiles = (c + kWideBT - 1) / kWideBT;
         TileInfo ti;
         ti.e = i;
-        ti.row0 = l + (rem % mtiles) * kWideBT;
+        ti.mt = rem % mtiles;
+        ti.row0 = l + ti.mt * kWideBT;
         ti.mrem = min(kWideBT, l + c - ti.row0);
         ti.n0 = (rem / mtiles) * cols;
         return ti;
@@ -293,12 +296,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // reads, so every stage issues the same loads.
     const char *pp[LPW];
     int p_left;
+    // L2 prefetch.  The four workgroups of an XCD that share a weight tile
+    // (its four token tiles, neighbours in the round robin) each touch a
+    // quarter of its rows kWidePfAhead stages before they are loaded, so the
+    // loads that follow hit in L2 instead of waiting on HBM.  Lane l covers
+    // half l / 16 % 2 of weight row 64 (mt % 4) + 16 wave + l % 16.
+    const char *pf;
+    int pf_rem;  // stages of the producer's segment from pf on
     auto produce_from = [&](int k) __attribute__((always_inline)) {
         const Segment sg = segment(min(k, n_seg - 1));
-        sources(tt.info(sg.tile, kCols), pp);
+        const TileInfo ti = tt.info(sg.tile, kCols);
+        sources(ti, pp);
 #pragma unroll
         for (int i = 0; i < LPW; ++i) pp[i] += (int64_t)sg.sb * 128;
         p_left = (k < n_seg) ? sg.se - sg.sb : 0x7fffffff;
+        const int r = 64 * (ti.mt & 3) + 16 * wave + (lane & 15);
+        const bf16_t *W = Wa;
+        int nr = ti.n0 + r;
+        if constexpr (SWIGLU) {
+            W = (r < BW / 2) ? Wa : Wb;
+            nr = ti.n0 + (r % (BW / 2));
+        }
+        nr = min(nr, N - 1);
+        pf = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + ((lane >> 4) & 1) * 64 +
+             (int64_t)sg.sb * 128;
+        pf_rem = sg.se - sg.sb;
+    };
+    // One prefetch per wave, after the loads of a stage (pf points at that
+    // stage): kWidePfAhead stages further, within the producer's segment
+    // (past the last segment the reloads stay within its first P stages).
+    auto prefetch = [&]() __attribute__((always_inline)) {
+        const int ahead = max(0, min(kWidePfAhead, pf_rem - 1));
+        --pf_rem;
+        __builtin_amdgcn_global_load_lds((const void *)(pf + ahead * 128),
+                                         (__attribute__((address_space(3))) void *)(smem + kWideP * kWideStageBytes),
+                                         4, 0, 0);
+        pf += 128;
     };
     int p_seg = 0;
     produce_from(0);
@@ -310,10 +343,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             dma16(pp[i], dst + (wave + kWideWaves * i) * 1024);
             pp[i] += 128;
         }
+        prefetch();
+        --p_left;
     }
-    p_left -= P;
     if (p_left == 0) produce_from(++p_seg);
-    wait_vmcnt_lgkm0<LPW * (P - 1)>();
+    // stage 0 has landed (stage 1's loads and prefetch may be in flight)
+    wait_vmcnt_lgkm0<(LPW + 1) * (P - 1)>();
     stage_barrier();
 
     int g = 0;  // stages consumed so far = ring cursor
@@ -351,7 +386,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             __builtin_amdgcn_sched_barrier(0);
             // Every read of this slot has landed and the next stage's loads
             // too (this wave's, then everyone's): free the slot.
-            wait_vmcnt_lgkm0<LPW * (P - 2)>();
+            // (the last prefetch may still be in flight: it was issued after
+            // those loads)
+            wait_vmcnt_lgkm0<(LPW + 1) * (P - 2) + 1>();
             stage_barrier();
             // Step 1 under the reads of the next stage's step 0 and the
             // loads refilling this slot P stages ahead: one read and one
@@ -366,6 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 mma_part(a1, b1, 3 * k, 3 * k + 3);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            prefetch();
             mma_part(a1, b1, 48, 64);
             __builtin_amdgcn_sched_barrier(0);
             // The reads above have landed by now; saying so keeps the
