@@ -373,39 +373,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         for (int s = cur.sb; s < cur.se; ++s, ++g) {
             const int slot = g % P;
-            // Step 0 under the reads of step 1, two MFMAs per read, so the
-            // last read still has 32 MFMAs to land under.
+            // Step 0 under the reads of step 1, one per MFMA, so the last
+            // read has 48 MFMAs to land under.
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                read_frag(a1, b1, slot, 1, k);
-                mma_part(a0, b0, 2 * k, 2 * k + 2);
+            for (int m = 0; m < 64; ++m) {
+                if (m < 16) read_frag(a1, b1, slot, 1, m);
+                mma_part(a0, b0, m, m + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            mma_part(a0, b0, 32, 64);
-            __builtin_amdgcn_sched_barrier(0);
             // Every read of this slot has landed and the next stage's loads
             // too (this wave's, then everyone's): free the slot.
             // (the last prefetch may still be in flight: it was issued after
             // those loads)
             wait_vmcnt_lgkm0<(LPW + 1) * (P - 2) + 1>();
             stage_barrier();
-            // Step 1 under the reads of the next stage's step 0 and the
-            // loads refilling this slot P stages ahead: one read and one
-            // load per three MFMAs, then 16 MFMAs for the last read to land.
-            static_assert(LPW == 16, "one load per fragment read");
+            // Step 1 under the reads of the next stage's step 0 (one per two
+            // MFMAs, so the last has 32 to land under) and the loads refilling
+            // this slot P stages ahead (one per four MFMAs, spread over the
+            // whole step so the load path never backs up into the issue).
+            static_assert(LPW == 16, "one load per four MFMAs");
             char *dst = smem + slot * kWideStageBytes;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                read_frag(a0, b0, (g + 1) % P, 0, k);
-                dma16(pp[k], dst + (wave + kWideWaves * k) * 1024);
-                pp[k] += 128;
-                mma_part(a1, b1, 3 * k, 3 * k + 3);
+            for (int m = 0; m < 64; ++m) {
+                if (m % 2 == 0 && m < 32) read_frag(a0, b0, (g + 1) % P, 0, m / 2);
+                if (m % 4 == 0) {
+                    dma16(pp[m / 4], dst + (wave + kWideWaves * (m / 4)) * 1024);
+                    pp[m / 4] += 128;
+                }
+                if (m == 63) prefetch();
+                mma_part(a1, b1, m, m + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            prefetch();
-            mma_part(a1, b1, 48, 64);
-            __builtin_amdgcn_sched_barrier(0);
             // The reads above have landed by now; saying so keeps the
             // compiler's next wait exact.
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
