@@ -67,7 +67,15 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *out, float v0, float v1, 
     *(uint2 *)out = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
 }
 
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + expf(-u)); }
+// silu(u) = u / (1 + e^-u) from the hardware base-2 exponential and
+// reciprocal (about 1 ulp each, a few ulp together: far inside bf16 and the
+// fp32 tolerances, and a fraction of the instructions of expf and an IEEE
+// division).  The limits come out right: u -> -inf gives 1 / inf = 0, and
+// u -> +inf gives e^-u = 0, so u itself.
+__device__ __forceinline__ float silu(float u) {
+    const float e = __builtin_amdgcn_exp2f(u * -1.4426950408889634f);  // -u log2(e)
+    return u * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // s_waitcnt constraining vmcnt to N and lgkmcnt to 0 (expcnt free); gfx9
 // encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8].
