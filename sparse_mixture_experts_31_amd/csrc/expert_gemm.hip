@@ -309,7 +309,7 @@ static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
     if (per_expert <= 32)
         return (dt == 1 && stream_supported(d, d_ff)) ? FfnPath::kStream : FfnPath::kSkinny;
     if (per_expert <= 256) return FfnPath::kGroupedSmall;
-    if (dt == 1 && wide_supported(d, d_ff)) return FfnPath::kWide;
+    if (dt == 1 && wide_supported(A, d, d_ff)) return FfnPath::kWide;
     return FfnPath::kGroupedLarge;
 }
 

@@ -160,7 +160,7 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
 // Wide-tile expert GEMMs (wide_gemm.hip), bf16 only.  `partial` (may be
 // NULL) is scratch for split tiles, at least wide_partial_bytes() bytes.
 size_t wide_partial_bytes();
-bool wide_supported(int d, int d_ff);
+bool wide_supported(int64_t A, int d, int d_ff);
 hipError_t launch_wide_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
                            const void *W1, const void *W3, const void *W2, int out_f32, int64_t A,
                            int d, int d_ff, int E, void *hbuf, void *out, float *partial,

@@ -221,31 +221,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         return sg;
     };
 
-    // Lane pointers of this wave's LPW 8-row loads of a tile: row r of a
-    // stage is loaded by wave (r / 8) % 4, lane 8 (r % 8) + chunk slot,
-    // fetching the chunk that belongs at that slot; every load instruction
-    // moves eight whole 128-byte lines.  Loads [0, LPW / 2) are weight rows,
-    // the rest token rows (act rows, through `gather` if set).
-    auto sources = [&](const TileInfo &ti, const char *(&src)[LPW]) {
+    // Sources of this wave's LPW 8-row loads of a tile: row r of a stage is
+    // loaded by wave (r / 8) % 4, lane 8 (r % 8) + chunk slot, fetching the
+    // chunk that belongs at that slot; every load instruction moves eight
+    // whole 128-byte lines.  Loads [0, LPW / 4) read base[0] (GEMM1: W1
+    // rows), [LPW / 4, LPW / 2) base[1] (the same W3 rows), the rest base[2]
+    // (token rows: act rows, through `gather` if set).  A load's address is a
+    // wave-uniform base plus a 32-bit lane offset, so the bases advance in
+    // scalar registers and the loads take the scalar-base address form.
+    auto sources = [&](const TileInfo &ti, const char *(&base)[3], uint32_t (&off)[LPW]) {
+        const bf16_t *W = Wa + ((int64_t)ti.e * N + ti.n0) * K;
+        base[0] = (const char *)W;
+        base[1] = SWIGLU ? (const char *)(Wb + ((int64_t)ti.e * N + ti.n0) * K) : base[0];
+        base[2] = (const char *)(act + (gather ? 0 : (int64_t)ti.row0 * act_ld));
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int r = (wave + kWideWaves * i) * 8 + (lane >> 3);
             const int c = (lane & 7) ^ ((r >> 1) & 7);
             if (i < LPW / 2) {
-                const bf16_t *W = Wa;
-                int nr;
-                if constexpr (SWIGLU) {
-                    W = (r < BW / 2) ? Wa : Wb;
-                    nr = ti.n0 + (r % (BW / 2));
-                } else {
-                    nr = ti.n0 + r;
-                }
-                nr = min(nr, N - 1);
-                src[i] = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + c * 16;
+                const int rr = SWIGLU ? r % (BW / 2) : r;  // row within the tile's rows of W
+                off[i] = (uint32_t)(min(ti.n0 + rr, N - 1) - ti.n0) * (uint32_t)(K * 2) + c * 16;
             } else {
                 const int row = act_row<8>(gather, ti.row0 + (wave + kWideWaves * i) * 8 - BW,
                                            ti.row0 + ti.mrem - 1, lane);
-                src[i] = (const char *)(act + (int64_t)row * act_ld) + c * 16;
+                off[i] = (uint32_t)(gather ? row : row - ti.row0) * (uint32_t)(act_ld * 2) + c * 16;
             }
         }
     };
@@ -294,55 +293,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // (whole tiles n_k >= P, split pieces multiples of P).  Past the last
     // segment it reloads the first stages of that segment, which nothing
     // reads, so every stage issues the same loads.
-    const char *pp[LPW];
+    const char *pb[3];   // wave-uniform bases of the producer's next stage
+    uint32_t po[LPW];    // lane offsets from them
     int p_left;
     // L2 prefetch.  The four workgroups of an XCD that share a weight tile
     // (its four token tiles, neighbours in the round robin) each touch a
     // quarter of its rows kWidePfAhead stages before they are loaded, so the
     // loads that follow hit in L2 instead of waiting on HBM.  Lane l covers
-    // half l / 16 % 2 of weight row 64 (mt % 4) + 16 wave + l % 16.
-    const char *pf;
-    int pf_rem;  // stages of the producer's segment from pf on
+    // half l / 16 % 2 of weight row 64 (mt % 4) + 16 wave + l % 16 (rows of
+    // one of W1 and W3 per wave).
+    const char *pfb;     // wave-uniform base of the stage the last loads went to
+    uint32_t pfo;
+    int pf_rem;          // stages of the producer's segment from pfb on
     auto produce_from = [&](int k) __attribute__((always_inline)) {
         const Segment sg = segment(min(k, n_seg - 1));
         const TileInfo ti = tt.info(sg.tile, kCols);
-        sources(ti, pp);
+        sources(ti, pb, po);
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) pp[i] += (int64_t)sg.sb * 128;
+        for (int b = 0; b < 3; ++b) pb[b] += (int64_t)sg.sb * 128;
         p_left = (k < n_seg) ? sg.se - sg.sb : 0x7fffffff;
-        const int r = 64 * (ti.mt & 3) + 16 * wave + (lane & 15);
-        const bf16_t *W = Wa;
-        int nr = ti.n0 + r;
-        if constexpr (SWIGLU) {
-            W = (r < BW / 2) ? Wa : Wb;
-            nr = ti.n0 + (r % (BW / 2));
-        }
-        nr = min(nr, N - 1);
-        pf = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + ((lane >> 4) & 1) * 64 +
-             (int64_t)sg.sb * 128;
+        const int r0 = 64 * (ti.mt & 3) + 16 * wave;  // wave-uniform; r0 % 16 == 0
+        const int r = r0 + (lane & 15);
+        const int rr = SWIGLU ? r % (BW / 2) : r;
+        pfb = (SWIGLU && r0 >= BW / 2) ? pb[1] : pb[0];
+        pfo = (uint32_t)(min(ti.n0 + rr, N - 1) - ti.n0) * (uint32_t)(K * 2) +
+              ((lane >> 4) & 1) * 64;
         pf_rem = sg.se - sg.sb;
     };
-    // One prefetch per wave, after the loads of a stage (pf points at that
+    // The loads of one stage into LDS slot dst, then the bases move on.
+    auto load_stage = [&](char *dst, int i) __attribute__((always_inline)) {
+        dma16(pb[i < LPW / 4 ? 0 : i < LPW / 2 ? 1 : 2] + po[i], dst + (wave + kWideWaves * i) * 1024);
+    };
+    auto advance = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < 3; ++b) pb[b] += 128;
+    };
+    // One prefetch per wave, after the loads of a stage (pfb is that
     // stage): kWidePfAhead stages further, within the producer's segment
     // (past the last segment the reloads stay within its first P stages).
     auto prefetch = [&]() __attribute__((always_inline)) {
         const int ahead = max(0, min(kWidePfAhead, pf_rem - 1));
         --pf_rem;
-        __builtin_amdgcn_global_load_lds((const void *)(pf + ahead * 128),
+        __builtin_amdgcn_global_load_lds((const void *)(pfb + ahead * 128 + pfo),
                                          (__attribute__((address_space(3))) void *)(smem + kWideP * kWideStageBytes),
                                          4, 0, 0);
-        pf += 128;
+        pfb += 128;
     };
     int p_seg = 0;
     produce_from(0);
 #pragma unroll
     for (int g = 0; g < P; ++g) {
-        char *dst = smem + g * kWideStageBytes;
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            dma16(pp[i], dst + (wave + kWideWaves * i) * 1024);
-            pp[i] += 128;
-        }
+        for (int i = 0; i < LPW; ++i) load_stage(smem + g * kWideStageBytes, i);
+        advance();
         prefetch();
         --p_left;
     }
@@ -397,11 +400,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int m = 0; m < 64; ++m) {
                 if (m % 2 == 0 && m < 32) read_frag(a0, b0, (g + 1) % P, 0, m / 2);
-                if (m % 4 == 0) {
-                    dma16(pp[m / 4], dst + (wave + kWideWaves * (m / 4)) * 1024);
-                    pp[m / 4] += 128;
+                if (m % 4 == 0) load_stage(dst, m / 4);
+                if (m == 63) {
+                    advance();
+                    prefetch();
                 }
-                if (m == 63) prefetch();
                 mma_part(a1, b1, m, m + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -532,8 +535,12 @@ hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, c
 
 size_t wide_partial_bytes() { return (size_t)2 * wide_grid() * kSlotFloats * sizeof(float); }
 
-bool wide_supported(int d, int d_ff) {
-    return d >= kWideP * kWideKStep && d_ff >= kWideP * kWideKStep;
+bool wide_supported(int64_t A, int d, int d_ff) {
+    // load addresses are 32-bit offsets from a tile's bases: token rows are
+    // found anywhere in x (at most A rows of d), weight rows within a tile
+    constexpr int64_t kOff = (int64_t)1 << 32;
+    return d >= kWideP * kWideKStep && d_ff >= kWideP * kWideKStep &&
+           A * d * 2 < kOff && (int64_t)kWideBW * std::max(d, d_ff) * 2 < kOff;
 }
 
 hipError_t launch_wide_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
