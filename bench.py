@@ -34,18 +34,24 @@ PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
 class HipEvents:
     """hipEvent_t handles from the HIP runtime (the library records them)."""
 
+    # Timing-only events: no system-scope fence (cache writeback and
+    # invalidate) when they complete, so recording them inside the timed
+    # loop costs the kernels around them nothing measurable.
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self) -> int:
         e = ctypes.c_void_p()
-        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
-            raise RuntimeError(f"hipEventCreate failed ({rc})")
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         return e.value
 
     def elapsed_ms(self, a: int, b: int) -> float:

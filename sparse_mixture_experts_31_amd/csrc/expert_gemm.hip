@@ -279,11 +279,9 @@ static hipError_t launch_grouped(const void *act, int64_t act_ld, const void *Wa
                                  void *out, int wg_per_cu, hipStream_t s) {
     using C = GemmCfg<BW, BT, WN, WM, P, SWIGLU, T>;
     auto kern = grouped_gemm_kernel<BW, BT, WN, WM, P, SWIGLU, T, TO>;
-    // LDS beyond the 64 KiB default must be requested per kernel (the call
-    // is cheap and keeps the library free of cached per-device state).
-    hipError_t err = hipFuncSetAttribute((const void *)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         C::kLdsBytes);
+    // LDS beyond the 64 KiB default must be requested per kernel
+    hipError_t err =
+        set_lds_limit<grouped_gemm_kernel<BW, BT, WN, WM, P, SWIGLU, T, TO>>(C::kLdsBytes);
     if (err != hipSuccess) return err;
     // Resident workgroups, a multiple of 8 (one share per XCD), and never
     // more than the tile count can use: sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1.

@@ -5,6 +5,7 @@
 #pragma once
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -139,6 +140,22 @@ struct TileInfo {
     int e, row0, mrem, n0;
     int mt;  // token tile index within its expert (wide_gemm.hip)
 };
+
+// Raises the dynamic LDS limit of kernel KERN, once per device: the runtime
+// call is not free, and made before every launch it shows as an idle gap
+// ahead of the kernel.  (One flag word per kernel instantiation.)
+template <auto KERN>
+static inline hipError_t set_lds_limit(int bytes) {
+    static std::atomic<unsigned long long> done{0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    err = hipFuncSetAttribute((const void *)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (err == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+    return err;
+}
 
 static inline int device_cus() {
     int dev = 0, cus = 0;

@@ -221,8 +221,7 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
                          void *out, hipStream_t s) {
     auto kern = stream_gemm_kernel<SWIGLU, TO>;
-    hipError_t err =
-        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kSLds);
+    hipError_t err = set_lds_limit<stream_gemm_kernel<SWIGLU, TO>>(kSLds);
     if (err != hipSuccess) return err;
     // one workgroup per CU, never more than there are tiles:
     // sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1

@@ -518,8 +518,7 @@ hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, c
                        const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
                        void *out, float *partial, hipStream_t s) {
     auto kern = wide_gemm_kernel<SWIGLU, TO>;
-    hipError_t err = hipFuncSetAttribute((const void *)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
+    hipError_t err = set_lds_limit<wide_gemm_kernel<SWIGLU, TO>>(kWideLds);
     if (err != hipSuccess) return err;
     const int grid = wide_grid();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), kWideLds, s, (const bf16_t *)act, act_ld,
