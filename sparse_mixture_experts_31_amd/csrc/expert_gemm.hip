@@ -305,7 +305,7 @@ enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide };
 static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
     const int64_t per_expert = A / E;
     if (per_expert <= 32)
-        return (dt == 1 && stream_supported(d, d_ff)) ? FfnPath::kStream : FfnPath::kSkinny;
+        return (dt == 1 && stream_supported(A, d, d_ff, E)) ? FfnPath::kStream : FfnPath::kSkinny;
     if (per_expert <= 256) return FfnPath::kGroupedSmall;
     if (dt == 1 && wide_supported(A, d, d_ff)) return FfnPath::kWide;
     return FfnPath::kGroupedLarge;

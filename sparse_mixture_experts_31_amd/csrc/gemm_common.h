@@ -168,7 +168,7 @@ static inline int device_cus() {
 
 // Weight-streaming expert GEMMs for decode-sized bf16 batches
 // (stream_gemm.hip).
-bool stream_supported(int d, int d_ff);
+bool stream_supported(int64_t A, int d, int d_ff, int E);
 hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
                              const void *W1, const void *W3, const void *W2, int out_f32,
                              int64_t A, int d, int d_ff, int E, void *hbuf, void *out,

@@ -6,67 +6,91 @@
 // Code listing), but at decode sizes every expert holds only a few rows
 // (about 8 at T = 32), so each weight byte feeds a handful of multiply-adds
 // and the kernel is a read of the active experts' weights at the HBM rate.
-// What it takes to stay at that rate:
-//  * bytes in flight: one persistent workgroup per CU runs a ring of P = 6
-//    LDS stages filled by global_load_lds, so ~120 KiB per CU are always on
-//    their way (a plain register double buffer keeps one stage in flight);
-//  * no drain between tiles: the ring runs across the tiles of a workgroup,
-//    the next tile's first stages load while the current one finishes;
-//  * non-temporal weight loads: weights are read once, and the nt hint lifts
-//    the sustained read rate (about 7 TB/s against about 6.2 on MI355X);
-//    token rows, shared by all tiles of an expert, keep the default policy.
+// What it takes to stay near that rate on MI355X:
+//  * few rows at a time, long pieces: HBM delivers 6.8-7.0 TB/s when a
+//    workgroup streams 16 weight rows in 1 KiB pieces, against 5.6-5.9 TB/s
+//    for 128-byte pieces of 128 rows (a probe of this ring's access
+//    pattern); so a stage is 16 rows x 1 KiB, one row per global_load_lds;
+//  * bytes in flight: one persistent workgroup per CU runs a 5-slot ring of
+//    those stages (64 KiB of weights always on their way) across tile
+//    boundaries, weight loads non-temporal (read once);
+//  * tokens reused, not re-streamed: a tile is 128 weight rows x 32 token
+//    rows walked as 512-wide K ranges, each K range as 8 stages of 16 rows
+//    (row group minor), so the token rows of a K range (32 x 1 KiB) are
+//    loaded once into one of two LDS buffers and read by all 8 stages.
+//    They are loaded with the weight loads of the previous K range's last
+//    four stages, when no stage still reads the buffer they go to.
 //
-// Tile: 128 weight rows (GEMM1: 64 rows of W1 and the same 64 rows of W3)
-// by 64 token rows of one expert, K in stages of 64 bf16.  A stage holds the
-// 128 weight rows and the 64 token rows (rows past the expert's count repeat
-// its last row and are not stored), 128 bytes each: every load instruction
-// moves eight whole 128-byte lines (with half lines per stage, the nt hint
-// can drop a line before the next stage reads its other half).  In LDS the
-// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7), which keeps the
-// 32-row operand reads free of bank conflicts.  Four waves in a 2 x 2 grid:
-// wave (wn, wm) multiplies the weight fragments of half wn (GEMM1: one W1
-// and the matching W3 fragment) with token fragment wm on
-// v_mfma_f32_32x32x16_bf16, two MFMAs per 16-wide k-step -- the matrix cores
-// idle almost always, by design.
+// Per stage each wave issues its 4 of the 16 weight rows (and, in the
+// second half of a K range, 2 of the next K range's token rows).  The load
+// counts follow the row group, so the loop body is unrolled over the 8 row
+// groups and every vmcnt wait is a compile-time constant.  A stage is
+// computed by the two waves of its row-group parity, one 16-token fragment
+// each, on v_mfma_f32_16x16x32_bf16: 16 MFMAs per stage per wave -- the
+// matrix cores idle almost always, by design.  In LDS the 16-byte chunk c
+// of a 1 KiB row r sits at chunk c ^ (r & 15), so the 16 rows of a fragment
+// read hit 16 distinct bank groups, and every load instruction is still one
+// contiguous row piece.
+//
+// Token rows are read in place (GEMM1 through `gather` = token_of): the map
+// is copied to LDS at the start, so a token row's address is one LDS read,
+// never a memory round trip in the middle of the ring.
 #include "gemm_common.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kSBW = 128, kSBT = 64, kSWaves = 4;
-constexpr int kSP = 6;                                // stages in the ring
-constexpr int kSRows = kSBW + kSBT;                   // LDS rows per stage
-constexpr int kSLPW = kSRows / 8 / kSWaves;           // 8-row loads per wave per stage
-constexpr int kSWLoads = kSBW / 8 / kSWaves;          // of which weight rows
-constexpr int kSStageBytes = kSRows * 128;
-constexpr int kSLds = kSP * kSStageBytes;
-constexpr int kSKStep = 64;                           // bf16 K elements per stage
-static_assert(kSRows % (8 * kSWaves) == 0 && kSBW % (8 * kSWaves) == 0, "load split");
-
-__device__ __forceinline__ int swz128(int r, int c) {
-    return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
-}
-static_assert(kSLPW * (kSP - 2) < 64, "vmcnt range");
+constexpr int kSRowsT = 128;   // weight rows per tile (GEMM1: 64 of W1 + the same 64 of W3)
+constexpr int kSBT = 32;       // token rows per tile
+constexpr int kSGrp = 16;      // weight rows per stage
+constexpr int kSGroups = kSRowsT / kSGrp;  // stages per K range
+constexpr int kSKRange = 512;  // bf16 K elements per row piece (1 KiB)
+constexpr int kSP = 5;         // weight stages in the ring
+constexpr int kSWStage = kSGrp * 1024;
+constexpr int kSTokBuf = kSBT * 1024;
+constexpr int kSMapMax = 33 * 64;  // token_of entries: A < 33 E on this path, E <= 64
+constexpr int kSLds = kSP * kSWStage + 2 * kSTokBuf + kSMapMax * 4;
 static_assert(kSLds <= 160 * 1024 - 1024, "LDS capacity");
+static_assert(kSGrp == 16 && kSGroups == 8, "one 16-row MFMA fragment per stage, 8 per K range");
+static_assert(kSP - 1 <= kSGroups / 2, "prologue stages carry no token loads");
+
+// Loads a wave issues along with stage row group rg: 4 weight rows, and in
+// the second half of a K range 2 token rows of the next one.
+constexpr int loads_of(int rg) { return 4 + (rg >= kSGroups / 2 ? 2 : 0); }
+// Loads that may still be in flight once stage rg's weights have landed:
+// the token loads issued with them and all loads of the next P - 2 stages.
+constexpr int vm_allow(int rg) {
+    int n = loads_of(rg) - 4;
+    for (int j = 1; j <= kSP - 2; ++j) n += loads_of((rg + j) % kSGroups);
+    return n;
+}
+static_assert(vm_allow(4) < 64, "vmcnt range");
+
+// Byte offset of 16-byte chunk c of 1 KiB row r in a buffer of such rows.
+__device__ __forceinline__ int swz1k(int r, int c) { return r * 1024 + ((c ^ (r & 15)) << 4); }
 
 }  // namespace
 
 template <bool SWIGLU, typename TO>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void stream_gemm_kernel(
     const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ gather,
     const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb,
     const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out) {
-    constexpr int P = kSP, LPW = kSLPW, BW = kSBW, BT = kSBT;
-    constexpr int kCols = SWIGLU ? BW / 2 : BW;  // output columns per tile
+    constexpr int P = kSP, G = kSGroups;
+    constexpr int kCols = SWIGLU ? kSRowsT / 2 : kSRowsT;  // output columns per tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
+    char *const wring = smem;
+    char *const tbuf = smem + P * kSWStage;
+    int32_t *const s_map = (int32_t *)(smem + P * kSWStage + 2 * kSTokBuf);
     __shared__ int s_lo[64], s_cnt[64], s_first[65];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    // wave-uniform by construction; saying so keeps the load bases scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int col_tiles = (N + kCols - 1) / kCols;
-    const int n_k = K / kSKStep;  // >= P - 1, checked by the launcher
+    const int n_kr = K / kSKRange;  // >= 1, checked by the launcher
 
     // Per-expert tile table (token tiles fastest, then column tiles); offsets
     // clamped to [0, A] so no row index leaves the buffers.
@@ -78,138 +102,202 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(
             s_lo[i] = lo;
             s_cnt[i] = hi - lo;
             s_first[i] = f;
-            f += (hi - lo + BT - 1) / BT * col_tiles;
+            f += (hi - lo + kSBT - 1) / kSBT * col_tiles;
         }
         s_first[E] = f;
     }
+    if (gather)
+        for (int i = tid; i < A; i += 256) s_map[i] = gather[i];
     __syncthreads();
-    const int total = s_first[E];
-    const int G = gridDim.x;
-    const int my_tiles = (total > (int)blockIdx.x) ? (total - (int)blockIdx.x + G - 1) / G : 0;
+    auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    const int total = u(s_first[E]);
+    const int NG = gridDim.x;
+    const int my_tiles = (total > (int)blockIdx.x) ? (total - (int)blockIdx.x + NG - 1) / NG : 0;
     if (my_tiles == 0) return;  // uniform over the workgroup
+    const int n_stages = my_tiles * n_kr * G;
 
     auto tile_info = [&](int k) {
-        const int t = (int)blockIdx.x + k * G;
+        const int t = (int)blockIdx.x + k * NG;
         int i = 0;
-        while (i + 1 < E && s_first[i + 1] <= t) ++i;
-        const int rem = t - s_first[i];
-        const int mtiles = (s_cnt[i] + BT - 1) / BT;
+        while (i + 1 < E && u(s_first[i + 1]) <= t) ++i;
+        const int rem = t - u(s_first[i]);
+        const int c = u(s_cnt[i]), l = u(s_lo[i]);
+        const int mtiles = (c + kSBT - 1) / kSBT;
         TileInfo ti;
         ti.e = i;
-        ti.row0 = s_lo[i] + (rem % mtiles) * BT;
-        ti.mrem = min(BT, s_lo[i] + s_cnt[i] - ti.row0);
+        ti.mt = rem % mtiles;
+        ti.row0 = l + ti.mt * kSBT;
+        ti.mrem = min(kSBT, l + c - ti.row0);
         ti.n0 = (rem / mtiles) * kCols;
         return ti;
     };
+    // Weight row r of a tile (GEMM1: r < 64 rows of W1, else the same rows of
+    // W3), clamped to the matrix.
+    auto weight_row = [&](const TileInfo &ti, int r) -> const char * {
+        const bf16_t *W = Wa;
+        int nr = ti.n0 + r;
+        if constexpr (SWIGLU) {
+            W = (r < kSRowsT / 2) ? Wa : Wb;
+            nr = ti.n0 + (r % (kSRowsT / 2));
+        }
+        nr = min(nr, N - 1);
+        return (const char *)(W + ((int64_t)ti.e * N + nr) * K);
+    };
+    // Token rows of a tile, one per lane: lane j < 32 holds the address of
+    // the tile's token row j (rows past the count repeat the last one), so a
+    // load of row j takes it with one readlane.
+    auto token_rows = [&](const TileInfo &ti) -> uint64_t {
+        const int r = ti.row0 + min(lane & (kSBT - 1), ti.mrem - 1);
+        const int row = gather ? s_map[r] : r;
+        return (uint64_t)(act + (int64_t)row * act_ld);
+    };
+    auto token_row = [&](uint64_t rows, int j) -> const char * {
+        return (const char *)(((uint64_t)__builtin_amdgcn_readlane((int)(rows >> 32), j) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)rows, j));
+    };
+    // One 1 KiB row piece of K range kr into LDS row dst (swizzle key `key`):
+    // lane l fetches the chunk that belongs at LDS chunk l.
+    auto piece = [&](const char *row, int kr, char *dst, int key, bool nt) {
+        const char *src = row + (int64_t)kr * 1024 + ((lane ^ key) << 4);
+        if (nt)
+            dma16_nt(src, dst);
+        else
+            dma16(src, dst);
+    };
 
-    // Lane pointers of this wave's LPW 8-row loads: load i covers stage rows
-    // (wave + 4 i) * 8 .. + 8, lane l the chunk that belongs at LDS offset
-    // 16 l; loads [0, kSWLoads) are weight rows, the rest token rows (act
-    // rows, through `gather` if set).
-    auto sources = [&](const TileInfo &ti, const char *(&src)[LPW]) {
+    // ---- producer: runs P - 1 stages ahead; stage pq goes to slot pq % P.
+    // (pk, pkr) are its tile and K range; past the last stage it keeps the
+    // last addresses, reloading into slots nothing reads.
+    int pk = 0, pkr = 0;
+    TileInfo pti = tile_info(0);
+    TileInfo pnext = my_tiles > 1 ? tile_info(1) : pti;
+    uint64_t prows = token_rows(pti), pnext_rows = token_rows(pnext);
+    auto issue = [&](int pq, int rg) __attribute__((always_inline)) {
+        char *slot = wring + (pq % P) * kSWStage;
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int r = (wave + kSWaves * i) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ((r >> 1) & 7);
-            if (i < kSWLoads) {
-                const bf16_t *W = Wa;
-                int nr;
-                if constexpr (SWIGLU) {
-                    W = (r < BW / 2) ? Wa : Wb;
-                    nr = ti.n0 + (r % (BW / 2));
-                } else {
-                    nr = ti.n0 + r;
-                }
-                nr = min(nr, N - 1);
-                src[i] = (const char *)(W + ((int64_t)ti.e * N + nr) * K) + c * 16;
-            } else {
-                const int row = act_row<8>(gather, ti.row0 + (wave + kSWaves * i) * 8 - BW,
-                                           ti.row0 + ti.mrem - 1, lane);
-                src[i] = (const char *)(act + (int64_t)row * act_ld) + c * 16;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * wave + i;  // row within the stage
+            piece(weight_row(pti, rg * kSGrp + r), pkr, slot + r * 1024, r, true);
+        }
+        if (rg >= G / 2) {
+            // token rows of the next K range (this tile's, or the next
+            // tile's first) into the buffer of that global K range
+            const bool last = (pkr + 1 == n_kr);
+            const uint64_t rows = last ? pnext_rows : prows;
+            char *tb = tbuf + ((pk * n_kr + pkr + 1) & 1) * kSTokBuf;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int j = 8 * (rg - G / 2) + 2 * wave + i;
+                piece(token_row(rows, j), last ? 0 : pkr + 1, tb + j * 1024, j & 15, false);
             }
         }
     };
-    auto issue = [&](int slot, const char *const (&src)[LPW], int stage) {
-        char *dst = smem + slot * kSStageBytes;
-        const int64_t off = (int64_t)stage * 128;
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            if (i < kSWLoads)
-                dma16_nt(src[i] + off, dst + (wave + kSWaves * i) * 1024);
-            else
-                dma16(src[i] + off, dst + (wave + kSWaves * i) * 1024);
+    // after the loads of a row group G - 1 stage: the next K range
+    auto next_range = [&](int pq_next) __attribute__((always_inline)) {
+        if (pq_next >= n_stages) return;
+        if (++pkr == n_kr) {
+            pkr = 0;
+            ++pk;
+            pti = pnext;
+            prows = pnext_rows;
+            pnext = (pk + 1 < my_tiles) ? tile_info(pk + 1) : pti;
+            pnext_rows = token_rows(pnext);
         }
     };
 
-    const int wn = wave & 1, wm = wave >> 1;
-    const int lrow = lane & 31, lhalf = lane >> 5;
-    // LDS rows of the wave's two weight fragments and its token fragment
-    const int wr0 = SWIGLU ? wn * 32 : wn * 64;
-    const int wr1 = SWIGLU ? BW / 2 + wn * 32 : wn * 64 + 32;
-    const int tr = BW + wm * 32;
-
-    const char *sc[LPW], *sn[LPW];  // sources of the current and the next tile
-    TileInfo nxt = tile_info(0);
-    sources(nxt, sn);
+    // prologue: the first K range's token rows, then stages 0 .. P - 2
 #pragma unroll
-    for (int g = 0; g < P - 1; ++g) issue(g, sn, g);
-
-    int g = 0;  // stages consumed so far = ring cursor
-    for (int c_k = 0; c_k < my_tiles; ++c_k) {
-        const TileInfo cur = nxt;
+    for (int i = 0; i < kSBT / 4; ++i) {
+        const int j = 8 * wave + i;
+        piece(token_row(prows, j), 0, tbuf + j * 1024, j & 15, false);
+    }
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) sc[i] = sn[i];
-        if (c_k + 1 < my_tiles) {
-            nxt = tile_info(c_k + 1);
-            sources(nxt, sn);
-        }
-        // (past the last tile sn == sc: the refills reload stages of this
-        // tile, which nothing reads)
-        f32x16 acc0 = {}, acc1 = {};
-        for (int s = 0; s < n_k; ++s, ++g) {
-            // stage g landed (this wave's loads, then everyone's); every wave
-            // is done reading the slot of stage g - 1
-            wait_vmcnt_lgkm0<LPW * (P - 2)>();
+    for (int q = 0; q < P - 1; ++q) issue(q, q);
+    int pq = P - 1;  // next stage the producer loads
+
+    // ---- consumer ----
+    const int par = wave >> 1, jfrag = wave & 1;  // row-group parity, token fragment
+    const int lr = lane & 15, lq = lane >> 4;
+    f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{};
+
+    int ck = 0, ckr = 0;
+    TileInfo cti = tile_info(0);
+    for (int s0 = 0; s0 < n_stages; s0 += G) {
+        const char *tb = tbuf + ((ck * n_kr + ckr) & 1) * kSTokBuf;
+        // the G stages of one K range, unrolled: every wait is a constant
+        auto stage = [&](auto rgc) __attribute__((always_inline)) {
+            constexpr int RG = decltype(rgc)::value;
+            constexpr int QRG = (RG + P - 1) % G;  // row group of the stage loaded now
+            // stage s0 + RG landed (this wave's loads, then everyone's), and
+            // every wave is done with the slot of the previous stage
+            wait_vmcnt_lgkm0<vm_allow(RG)>();
             stage_barrier();
-            const int q = s + P - 1;
-            if (q < n_k)
-                issue((g + P - 1) % P, sc, q);
-            else
-                issue((g + P - 1) % P, sn, q - n_k);
-            const char *base = smem + (g % P) * kSStageBytes;
+            issue(pq, QRG);
+            if (QRG == G - 1) next_range(pq + 1);
+            ++pq;
+            // the two waves of this row group's parity, one token fragment each
+            // (the fragment reads run RD k-steps ahead of the MFMAs, which
+            // alternate between two accumulators; scheduling barriers keep
+            // that order)
+            if ((RG & 1) == par) {
+                constexpr int NT = kSKRange / 32, RD = 3;
+                const char *wslot = wring + ((s0 + RG) % P) * kSWStage;
+                i32x4 w[NT], x[NT];
+                auto rd = [&](int t) __attribute__((always_inline)) {
+                    const int c = 4 * t + lq;
+                    w[t] = *(const i32x4 *)(wslot + swz1k(lr, c));
+                    x[t] = *(const i32x4 *)(tb + swz1k(16 * jfrag + lr, c));
+                };
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int c = 2 * t + lhalf;
-                const i32x4 w0 = *(const i32x4 *)(base + swz128(wr0 + lrow, c));
-                const i32x4 w1 = *(const i32x4 *)(base + swz128(wr1 + lrow, c));
-                const i32x4 x = *(const i32x4 *)(base + swz128(tr + lrow, c));
-                acc0 = mma_step<bf16_t>(w0, x, acc0);
-                acc1 = mma_step<bf16_t>(w1, x, acc1);
+                for (int t = 0; t < RD; ++t) rd(t);
+                f32x4 ab[2] = {acc[RG >> 1], f32x4{}};
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    if (t + RD < NT) rd(t + RD);
+                    ab[t & 1] = mma16(w[t], x[t], ab[t & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                acc[RG >> 1] = ab[0] + ab[1];
             }
-        }
-        // Epilogue: element q of a fragment is D[n = 8 (q / 4) + 4 lhalf + q % 4][m = lrow].
-        const int m = wm * 32 + lrow;
-        if (m < cur.mrem) {
-            TO *orow = out + (int64_t)(cur.row0 + m) * N;
+        };
+        stage(std::integral_constant<int, 0>{});
+        stage(std::integral_constant<int, 1>{});
+        stage(std::integral_constant<int, 2>{});
+        stage(std::integral_constant<int, 3>{});
+        stage(std::integral_constant<int, 4>{});
+        stage(std::integral_constant<int, 5>{});
+        stage(std::integral_constant<int, 6>{});
+        stage(std::integral_constant<int, 7>{});
+        if (++ckr < n_kr) continue;
+
+        // Epilogue of tile ck.  Wave (par, jfrag) holds row groups par + 2 h
+        // (h = 0..3) for tokens 16 jfrag .. + 16: lane l has weight rows
+        // 4 (l / 16) .. + 4 of a group, for token l % 16.  GEMM1: groups
+        // par, par + 2 are W1 rows, par + 4, par + 6 the same W3 rows.
+        const int m = 16 * jfrag + lr;
+        if (m < cti.mrem) {
+            TO *orow = out + (int64_t)(cti.row0 + m) * N;
 #pragma unroll
-            for (int f = 0; f < (SWIGLU ? 1 : 2); ++f) {
+            for (int h = 0; h < (SWIGLU ? 2 : 4); ++h) {
+                const int n = cti.n0 + 16 * (par + 2 * h) + 4 * lq;
+                if (n < N) {
+                    float r[4];
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int n = cur.n0 + (SWIGLU ? wn * 32 : wn * 64 + f * 32) + 8 * gq + 4 * lhalf;
-                    if (n < N) {
-                        float r[4];
-#pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) {
-                            if constexpr (SWIGLU)
-                                r[qq] = silu(acc0[4 * gq + qq]) * acc1[4 * gq + qq];
-                            else
-                                r[qq] = (f == 0 ? acc0 : acc1)[4 * gq + qq];
-                        }
-                        store4<TO>(orow + n, r[0], r[1], r[2], r[3]);
+                    for (int q = 0; q < 4; ++q) {
+                        r[q] = acc[h][q];
+                        if constexpr (SWIGLU) r[q] = silu(r[q]) * acc[h + 2][q];
                     }
+                    store4<TO>(orow + n, r[0], r[1], r[2], r[3]);
                 }
             }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = f32x4{};
+        ckr = 0;
+        if (++ck < my_tiles) cti = tile_info(ck);
     }
     wait_vmcnt_lgkm0<0>();  // the trailing reloads land before the wave ends
 }
@@ -220,24 +308,25 @@ template <bool SWIGLU, typename TO>
 hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
                          void *out, hipStream_t s) {
-    auto kern = stream_gemm_kernel<SWIGLU, TO>;
     hipError_t err = set_lds_limit<stream_gemm_kernel<SWIGLU, TO>>(kSLds);
     if (err != hipSuccess) return err;
     // one workgroup per CU, never more than there are tiles:
     // sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1
-    const int64_t cols = SWIGLU ? kSBW / 2 : kSBW;
+    const int64_t cols = SWIGLU ? kSRowsT / 2 : kSRowsT;
     const int64_t tile_bound = (N + cols - 1) / cols * ((A + kSBT - 1) / kSBT + E - 1);
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), tile_bound));
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), kSLds, s, (const bf16_t *)act, act_ld,
-                       gather, (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
-                       (TO *)out);
+    hipLaunchKernelGGL((stream_gemm_kernel<SWIGLU, TO>), dim3(grid), dim3(256), kSLds, s,
+                       (const bf16_t *)act, act_ld, gather, (const bf16_t *)Wa,
+                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool stream_supported(int d, int d_ff) {
-    return d >= (kSP - 1) * kSKStep && d_ff >= (kSP - 1) * kSKStep;
+bool stream_supported(int64_t A, int d, int d_ff, int E) {
+    // whole 1 KiB row pieces, and the token map fits its LDS area
+    return d % kSKRange == 0 && d_ff % kSKRange == 0 && d >= kSKRange && d_ff >= kSKRange &&
+           A <= kSMapMax && E <= 64;
 }
 
 hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,

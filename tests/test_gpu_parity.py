@@ -58,10 +58,14 @@ SMALL = [
     # shortest k-loop (d = 128) and a W2 tile half past N
     Workload("wide-many", 18, T=2048, d=128, d_ff=2304),
     # every token takes both of two experts: 300 rows each, a full 256-row
-    # tile and a narrow one of 44 rows (the quarter-MFMA k-loop)
+    # tile and a ragged one of 44 rows
     Workload("wide-narrow", 19, T=300, d=256, d_ff=512, E=2, k=2),
-    # ~300 rows per expert from a random split: narrow last tiles again
+    # ~300 rows per expert from a random split: ragged last tiles again
     Workload("wide-narrow-k1", 22, T=600, d=192, d_ff=640, E=2, k=1),
+    # decode-sized on the weight-streaming kernels with more tiles than
+    # workgroups (the ring crosses tile boundaries), 2 K ranges of 512 in
+    # GEMM1 and 10 in GEMM2
+    Workload("stream-tiles", 23, T=24, d=1024, d_ff=5120),
 ]
 
 
@@ -176,9 +180,9 @@ def test_pieces_expert_ffn_and_combine():
 
 @pytest.mark.parametrize("w", [
     Workload("forced", 20, T=200, d=256, d_ff=512),
-    # decode-sized (T*k/E <= 32): the weight-streaming kernels, here with two
-    # token tiles for each of the two experts
-    Workload("forced-stream", 21, T=128, d=384, d_ff=768),
+    # decode-sized (T*k/E <= 32): the weight-streaming kernels, here with four
+    # token tiles of 32 rows for each of the two experts
+    Workload("forced-stream", 21, T=128, d=512, d_ff=1024),
 ], ids=lambda w: w.name)
 def test_all_tokens_to_two_experts_and_untouched_experts(w):
     """Every token routes to experts 3 and 5; the other six get no rows, and
