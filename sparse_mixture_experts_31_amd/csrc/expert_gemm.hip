@@ -326,7 +326,8 @@ static hipError_t launch_ffn_typed(const void *act, const int32_t *gather,
     switch (path) {
         case FfnPath::kStream:
             return launch_stream_ffn(act, gather, offsets, W1, W3, W2, ElemSize<TO>::value == 4,
-                                     A, d, d_ff, E, hbuf, out, mid, s);
+                                     A, d, d_ff, E, hbuf, out, (float *)scratch, scratch_bytes,
+                                     mid, s);
         case FfnPath::kSkinny:
             return moe_launch_skinny_ffn(act, offsets, W1, W3, W2, dt, ElemSize<TO>::value == 4, A,
                                          d, d_ff, E, hbuf, out, mid, s);
@@ -360,8 +361,14 @@ bool moe_expert_ffn_gathers(int dt, int64_t A, int d, int d_ff, int E) {
 }
 
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E) {
-    if (moe::ffn_path(dt, A, d, d_ff, E) != moe::FfnPath::kWide) return 0;
-    return moe::wide_partial_bytes();
+    switch (moe::ffn_path(dt, A, d, d_ff, E)) {
+        case moe::FfnPath::kWide:
+            return moe::wide_partial_bytes();
+        case moe::FfnPath::kStream:
+            return moe::stream_partial_bytes(A, d, d_ff, E);
+        default:
+            return 0;
+    }
 }
 
 hipError_t moe_launch_expert_ffn(const void *act, const int32_t *gather, const int32_t *offsets,

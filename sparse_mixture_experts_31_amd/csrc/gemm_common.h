@@ -168,11 +168,15 @@ static inline int device_cus() {
 
 // Weight-streaming expert GEMMs for decode-sized bf16 batches
 // (stream_gemm.hip).
+// `partial` (may be NULL) is scratch for the K chunks of GEMM2 at the
+// smallest batches, at least stream_partial_bytes() bytes (0: none used).
 bool stream_supported(int64_t A, int d, int d_ff, int E);
+size_t stream_partial_bytes(int64_t A, int d, int d_ff, int E);
 hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
                              const void *W1, const void *W3, const void *W2, int out_f32,
                              int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
-                             hipEvent_t mid, hipStream_t s);
+                             float *partial, size_t partial_bytes, hipEvent_t mid,
+                             hipStream_t s);
 
 // Wide-tile expert GEMMs (wide_gemm.hip), bf16 only.  `partial` (may be
 // NULL) is scratch for split tiles, at least wide_partial_bytes() bytes.

@@ -76,7 +76,8 @@ template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void stream_gemm_kernel(
     const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ gather,
     const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb,
-    const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out) {
+    const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out,
+    int kc, float *__restrict__ part) {
     constexpr int P = kSP, G = kSGroups;
     constexpr int kCols = SWIGLU ? kSRowsT / 2 : kSRowsT;  // output columns per tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -110,26 +111,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = tid; i < A; i += 256) s_map[i] = gather[i];
     __syncthreads();
     auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-    const int total = u(s_first[E]);
+    // Work items: tile t's K ranges cut into kc contiguous chunks (kc > 1
+    // only for GEMM2 at the smallest batches, where whole tiles would leave
+    // CUs idle); item w = kc t + chunk, taken round robin.
+    const int total = u(s_first[E]) * kc;
     const int NG = gridDim.x;
-    const int my_tiles = (total > (int)blockIdx.x) ? (total - (int)blockIdx.x + NG - 1) / NG : 0;
-    if (my_tiles == 0) return;  // uniform over the workgroup
-    const int n_stages = my_tiles * n_kr * G;
+    const int my_items = (total > (int)blockIdx.x) ? (total - (int)blockIdx.x + NG - 1) / NG : 0;
+    if (my_items == 0) return;  // uniform over the workgroup
 
-    auto tile_info = [&](int k) {
-        const int t = (int)blockIdx.x + k * NG;
+    struct Item {
+        TileInfo ti;
+        int kr0, kr1, chunk;  // K ranges [kr0, kr1) of the tile
+    };
+    auto item_info = [&](int k) {
+        const int w = (int)blockIdx.x + k * NG;
+        const int t = w / kc;
+        Item it;
+        it.chunk = w - t * kc;
+        it.kr0 = it.chunk * n_kr / kc;
+        it.kr1 = (it.chunk + 1) * n_kr / kc;
         int i = 0;
         while (i + 1 < E && u(s_first[i + 1]) <= t) ++i;
         const int rem = t - u(s_first[i]);
         const int c = u(s_cnt[i]), l = u(s_lo[i]);
         const int mtiles = (c + kSBT - 1) / kSBT;
-        TileInfo ti;
+        TileInfo &ti = it.ti;
         ti.e = i;
         ti.mt = rem % mtiles;
         ti.row0 = l + ti.mt * kSBT;
         ti.mrem = min(kSBT, l + c - ti.row0);
         ti.n0 = (rem / mtiles) * kCols;
-        return ti;
+        return it;
     };
     // Weight row r of a tile (GEMM1: r < 64 rows of W1, else the same rows of
     // W3), clamped to the matrix.
@@ -168,40 +180,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ---- producer: runs P - 1 stages ahead; stage pq goes to slot pq % P.
     // (pk, pkr) are its tile and K range; past the last stage it keeps the
     // last addresses, reloading into slots nothing reads.
-    int pk = 0, pkr = 0;
-    TileInfo pti = tile_info(0);
-    TileInfo pnext = my_tiles > 1 ? tile_info(1) : pti;
-    uint64_t prows = token_rows(pti), pnext_rows = token_rows(pnext);
+    // (pk, pkr): the producer's item and K range; pr counts the K ranges it
+    // has entered (token buffer pr % 2).
+    Item pit = item_info(0);
+    Item pnext = my_items > 1 ? item_info(1) : pit;
+    int pk = 0, pkr = pit.kr0, pr = 0;
+    uint64_t prows = token_rows(pit.ti), pnext_rows = token_rows(pnext.ti);
     auto issue = [&](int pq, int rg) __attribute__((always_inline)) {
         char *slot = wring + (pq % P) * kSWStage;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * wave + i;  // row within the stage
-            piece(weight_row(pti, rg * kSGrp + r), pkr, slot + r * 1024, r, true);
+            piece(weight_row(pit.ti, rg * kSGrp + r), pkr, slot + r * 1024, r, true);
         }
         if (rg >= G / 2) {
-            // token rows of the next K range (this tile's, or the next
-            // tile's first) into the buffer of that global K range
-            const bool last = (pkr + 1 == n_kr);
+            // token rows of the next K range (this item's, or the next
+            // item's first) into the other buffer
+            const bool last = (pkr + 1 == pit.kr1);
             const uint64_t rows = last ? pnext_rows : prows;
-            char *tb = tbuf + ((pk * n_kr + pkr + 1) & 1) * kSTokBuf;
+            const int nkr = last ? pnext.kr0 : pkr + 1;
+            char *tb = tbuf + ((pr + 1) & 1) * kSTokBuf;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int j = 8 * (rg - G / 2) + 2 * wave + i;
-                piece(token_row(rows, j), last ? 0 : pkr + 1, tb + j * 1024, j & 15, false);
+                piece(token_row(rows, j), nkr, tb + j * 1024, j & 15, false);
             }
         }
     };
-    // after the loads of a row group G - 1 stage: the next K range
-    auto next_range = [&](int pq_next) __attribute__((always_inline)) {
-        if (pq_next >= n_stages) return;
-        if (++pkr == n_kr) {
-            pkr = 0;
+    // after the loads of a row group G - 1 stage: the next K range (past
+    // the last one the producer stays, reloading it into slots nothing reads)
+    auto next_range = [&]() __attribute__((always_inline)) {
+        if (pkr + 1 < pit.kr1) {
+            ++pkr;
+            ++pr;
+        } else if (pk + 1 < my_items) {
             ++pk;
-            pti = pnext;
+            ++pr;
+            pit = pnext;
+            pkr = pit.kr0;
             prows = pnext_rows;
-            pnext = (pk + 1 < my_tiles) ? tile_info(pk + 1) : pti;
-            pnext_rows = token_rows(pnext);
+            pnext = (pk + 1 < my_items) ? item_info(pk + 1) : pit;
+            pnext_rows = token_rows(pnext.ti);
         }
     };
 
@@ -209,8 +228,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < kSBT / 4; ++i) {
         const int j = 8 * wave + i;
-        piece(token_row(prows, j), 0, tbuf + j * 1024, j & 15, false);
+        piece(token_row(prows, j), pit.kr0, tbuf + j * 1024, j & 15, false);
     }
+    static_assert(P - 1 < G, "the prologue stays in the first K range");
 #pragma unroll
     for (int q = 0; q < P - 1; ++q) issue(q, q);
     int pq = P - 1;  // next stage the producer loads
@@ -222,106 +242,148 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x4{};
 
-    int ck = 0, ckr = 0;
-    TileInfo cti = tile_info(0);
-    for (int s0 = 0; s0 < n_stages; s0 += G) {
-        const char *tb = tbuf + ((ck * n_kr + ckr) & 1) * kSTokBuf;
-        // the G stages of one K range, unrolled: every wait is a constant
-        auto stage = [&](auto rgc) __attribute__((always_inline)) {
-            constexpr int RG = decltype(rgc)::value;
-            constexpr int QRG = (RG + P - 1) % G;  // row group of the stage loaded now
-            // stage s0 + RG landed (this wave's loads, then everyone's), and
-            // every wave is done with the slot of the previous stage
-            wait_vmcnt_lgkm0<vm_allow(RG)>();
-            stage_barrier();
-            issue(pq, QRG);
-            if (QRG == G - 1) next_range(pq + 1);
-            ++pq;
-            // the two waves of this row group's parity, one token fragment each
-            // (the fragment reads run RD k-steps ahead of the MFMAs, which
-            // alternate between two accumulators; scheduling barriers keep
-            // that order)
-            if ((RG & 1) == par) {
-                constexpr int NT = kSKRange / 32, RD = 3;
-                const char *wslot = wring + ((s0 + RG) % P) * kSWStage;
-                i32x4 w[NT], x[NT];
-                auto rd = [&](int t) __attribute__((always_inline)) {
-                    const int c = 4 * t + lq;
-                    w[t] = *(const i32x4 *)(wslot + swz1k(lr, c));
-                    x[t] = *(const i32x4 *)(tb + swz1k(16 * jfrag + lr, c));
-                };
+    int cr = 0;  // K ranges consumed (token buffer cr % 2, ring stage G cr + rg)
+    for (int ck = 0; ck < my_items; ++ck) {
+        const Item cit = item_info(ck);
+        const TileInfo &cti = cit.ti;
+        for (int ckr = cit.kr0; ckr < cit.kr1; ++ckr, ++cr) {
+            const char *tb = tbuf + (cr & 1) * kSTokBuf;
+            const int s0 = cr * G;
+            // the G stages of one K range, unrolled: every wait is a constant
+            auto stage = [&](auto rgc) __attribute__((always_inline)) {
+                constexpr int RG = decltype(rgc)::value;
+                constexpr int QRG = (RG + P - 1) % G;  // row group of the stage loaded now
+                // stage s0 + RG landed (this wave's loads, then everyone's),
+                // and every wave is done with the slot of the previous stage
+                wait_vmcnt_lgkm0<vm_allow(RG)>();
+                stage_barrier();
+                issue(pq, QRG);
+                if (QRG == G - 1) next_range();
+                ++pq;
+                // the two waves of this row group's parity, one token fragment
+                // each (the fragment reads run RD k-steps ahead of the MFMAs,
+                // which alternate between two accumulators)
+                if ((RG & 1) == par) {
+                    constexpr int NT = kSKRange / 32, RD = 3;
+                    const char *wslot = wring + ((s0 + RG) % P) * kSWStage;
+                    i32x4 w[NT], x[NT];
+                    auto rd = [&](int t) __attribute__((always_inline)) {
+                        const int c = 4 * t + lq;
+                        w[t] = *(const i32x4 *)(wslot + swz1k(lr, c));
+                        x[t] = *(const i32x4 *)(tb + swz1k(16 * jfrag + lr, c));
+                    };
 #pragma unroll
-                for (int t = 0; t < RD; ++t) rd(t);
-                f32x4 ab[2] = {acc[RG >> 1], f32x4{}};
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    if (t + RD < NT) rd(t + RD);
-                    ab[t & 1] = mma16(w[t], x[t], ab[t & 1]);
+                    for (int t = 0; t < RD; ++t) rd(t);
+                    f32x4 ab[2] = {acc[RG >> 1], f32x4{}};
                     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        if (t + RD < NT) rd(t + RD);
+                        ab[t & 1] = mma16(w[t], x[t], ab[t & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    acc[RG >> 1] = ab[0] + ab[1];
                 }
-                acc[RG >> 1] = ab[0] + ab[1];
-            }
-        };
-        stage(std::integral_constant<int, 0>{});
-        stage(std::integral_constant<int, 1>{});
-        stage(std::integral_constant<int, 2>{});
-        stage(std::integral_constant<int, 3>{});
-        stage(std::integral_constant<int, 4>{});
-        stage(std::integral_constant<int, 5>{});
-        stage(std::integral_constant<int, 6>{});
-        stage(std::integral_constant<int, 7>{});
-        if (++ckr < n_kr) continue;
+            };
+            stage(std::integral_constant<int, 0>{});
+            stage(std::integral_constant<int, 1>{});
+            stage(std::integral_constant<int, 2>{});
+            stage(std::integral_constant<int, 3>{});
+            stage(std::integral_constant<int, 4>{});
+            stage(std::integral_constant<int, 5>{});
+            stage(std::integral_constant<int, 6>{});
+            stage(std::integral_constant<int, 7>{});
+        }
 
-        // Epilogue of tile ck.  Wave (par, jfrag) holds row groups par + 2 h
+        // Epilogue of the item.  Wave (par, jfrag) holds row groups par + 2 h
         // (h = 0..3) for tokens 16 jfrag .. + 16: lane l has weight rows
         // 4 (l / 16) .. + 4 of a group, for token l % 16.  GEMM1: groups
-        // par, par + 2 are W1 rows, par + 4, par + 6 the same W3 rows.
+        // par, par + 2 are W1 rows, par + 4, par + 6 the same W3 rows.  A
+        // K chunk of a tile (kc > 1, GEMM2) leaves its fp32 sums in its slice
+        // of `part` for stream_reduce_kernel.
         const int m = 16 * jfrag + lr;
         if (m < cti.mrem) {
-            TO *orow = out + (int64_t)(cti.row0 + m) * N;
+            const int64_t row = cti.row0 + m;
 #pragma unroll
             for (int h = 0; h < (SWIGLU ? 2 : 4); ++h) {
                 const int n = cti.n0 + 16 * (par + 2 * h) + 4 * lq;
                 if (n < N) {
-                    float r[4];
+                    if (!SWIGLU && kc > 1) {
+                        *(f32x4 *)(part + ((int64_t)cit.chunk * A + row) * N + n) = acc[h];
+                    } else {
+                        float r[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        r[q] = acc[h][q];
-                        if constexpr (SWIGLU) r[q] = silu(r[q]) * acc[h + 2][q];
+                        for (int q = 0; q < 4; ++q) {
+                            r[q] = acc[h][q];
+                            if constexpr (SWIGLU) r[q] = silu(r[q]) * acc[h + 2][q];
+                        }
+                        store4<TO>(out + row * N + n, r[0], r[1], r[2], r[3]);
                     }
-                    store4<TO>(orow + n, r[0], r[1], r[2], r[3]);
                 }
             }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = f32x4{};
-        ckr = 0;
-        if (++ck < my_tiles) cti = tile_info(ck);
     }
     wait_vmcnt_lgkm0<0>();  // the trailing reloads land before the wave ends
 }
 
+// out[i] = sum over the kc slices of part[s][i], in slice order (the K
+// chunks of a GEMM2 tile, so the sum is the same on every run).
+template <typename TO>
+__global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restrict__ part,
+                                                            int kc, int64_t n4,
+                                                            TO *__restrict__ out) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * 256) {
+        f32x4 r = ((const f32x4 *)part)[i];
+        for (int c = 1; c < kc; ++c) r += ((const f32x4 *)part)[c * n4 + i];
+        store4<TO>(out + 4 * i, r[0], r[1], r[2], r[3]);
+    }
+}
+
 namespace {
+
+// K chunks per GEMM2 tile: at the smallest batches (fewer than two rows per
+// expert on average) the GEMM2 tiles, at most min(E, A) experts x ceil(d /
+// 128), leave CUs idle; cutting each tile's K ranges into chunks gives
+// every CU about two items.  Otherwise 1.
+int stream_chunks(int64_t A, int d, int d_ff, int E) {
+    if (A <= 0 || A >= 2 * (int64_t)E) return 1;
+    const int64_t tiles = std::min<int64_t>(E, A) * ((d + kSRowsT - 1) / kSRowsT);
+    if (tiles <= 0) return 1;
+    const int64_t kc = (2 * (int64_t)device_cus() + tiles - 1) / tiles;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(kc, d_ff / kSKRange));
+}
 
 template <bool SWIGLU, typename TO>
 hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
-                         void *out, hipStream_t s) {
+                         void *out, int kc, float *part, hipStream_t s) {
     hipError_t err = set_lds_limit<stream_gemm_kernel<SWIGLU, TO>>(kSLds);
     if (err != hipSuccess) return err;
-    // one workgroup per CU, never more than there are tiles:
-    // sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1
+    // one workgroup per CU, never more than there are items:
+    // sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1 tiles, kc items each
     const int64_t cols = SWIGLU ? kSRowsT / 2 : kSRowsT;
-    const int64_t tile_bound = (N + cols - 1) / cols * ((A + kSBT - 1) / kSBT + E - 1);
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), tile_bound));
+    const int64_t item_bound = (N + cols - 1) / cols * ((A + kSBT - 1) / kSBT + E - 1) * kc;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), item_bound));
     hipLaunchKernelGGL((stream_gemm_kernel<SWIGLU, TO>), dim3(grid), dim3(256), kSLds, s,
                        (const bf16_t *)act, act_ld, gather, (const bf16_t *)Wa,
-                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out);
+                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, kc, part);
+    if ((err = hipGetLastError()) != hipSuccess || kc == 1) return err;
+    const int64_t n4 = A * N / 4;  // N is a multiple of 512
+    const int rgrid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
+    hipLaunchKernelGGL((stream_reduce_kernel<TO>), dim3(rgrid), dim3(256), 0, s,
+                       (const float *)part, kc, n4, (TO *)out);
     return hipGetLastError();
 }
 
 }  // namespace
+
+size_t stream_partial_bytes(int64_t A, int d, int d_ff, int E) {
+    const int kc = stream_chunks(A, d, d_ff, E);
+    return kc > 1 ? (size_t)kc * A * d * sizeof(float) : 0;
+}
 
 bool stream_supported(int64_t A, int d, int d_ff, int E) {
     // whole 1 KiB row pieces, and the token map fits its LDS area
@@ -332,16 +394,20 @@ bool stream_supported(int64_t A, int d, int d_ff, int E) {
 hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
                              const void *W1, const void *W3, const void *W2, int out_f32,
                              int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
-                             hipEvent_t mid, hipStream_t s) {
-    hipError_t err =
-        launch_stream<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A, hbuf, s);
+                             float *partial, size_t partial_bytes, hipEvent_t mid,
+                             hipStream_t s) {
+    hipError_t err = launch_stream<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A,
+                                                 hbuf, 1, nullptr, s);
     if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
     if (err != hipSuccess) return err;
+    // GEMM2 in K chunks when the scratch for their partial sums is there
+    int kc = stream_chunks(A, d, d_ff, E);
+    if (kc > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) kc = 1;
     if (out_f32)
         return launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff,
-                                           A, out, s);
+                                           A, out, kc, partial, s);
     return launch_stream<false, bf16_t>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff, A,
-                                        out, s);
+                                        out, kc, partial, s);
 }
 
 }  // namespace moe
