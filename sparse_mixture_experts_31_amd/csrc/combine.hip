@@ -3,7 +3,8 @@
 // combine_kernel: y = sum_j g_j E_j(x) (tokentrails lineage, step "Two
 //   experts per token": y = ga.Ea(x) + gb.Eb(x)), optionally plus a residual
 //   (the block's h + moe(...), tokentrails Code listing).  One wave per
-//   token; each lane handles 8 consecutive elements per step with 16-byte
+//   512-element piece of a token's row, so even a handful of tokens spread
+//   over many waves; each lane handles 8 consecutive elements with 16-byte
 //   loads, sums in fp32 in slot order and rounds once.
 // rmsnorm_kernel: h / sqrt(mean(h^2) + eps) with unit gain (tokentrails Code
 //   listing; the block is LLaMA's).  The sum of squares and the scale are
@@ -49,6 +50,7 @@ struct Vec8<float> {
 };
 
 constexpr int kRowWaves = 4;
+constexpr int kCombinePiece = kWave * 8;  // elements of a row per combine wave
 
 // TI: type of the expert outputs (the activation type, or fp32 when the
 // fused layer keeps them unrounded); T: residual and output type.
@@ -57,8 +59,11 @@ __global__ __launch_bounds__(kRowWaves *kWave) void combine_kernel(
     const TI *__restrict__ out_perm, const int32_t *__restrict__ row_of,
     const float *__restrict__ gw, const T *residual, int64_t T_, int d, int k, T *y) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kRowWaves + threadIdx.x / kWave;
-    if (t >= T_) return;
+    const int nch = (d + kCombinePiece - 1) / kCombinePiece;  // pieces per row
+    const int64_t wv = (int64_t)blockIdx.x * kRowWaves + threadIdx.x / kWave;
+    const int64_t t = wv / nch;
+    const int i = (int)(wv - t * nch) * kCombinePiece + lane * 8;
+    if (t >= T_ || i >= d) return;
     int rows[8];
     float g[8];
 #pragma unroll
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(kRowWaves *kWave) void combine_kernel(
         rows[j] = (j < k) ? row_of[t * k + j] : -1;
         g[j] = (j < k) ? gw[t * k + j] : 0.f;
     }
-    for (int i = lane * 8; i < d; i += kWave * 8) {
+    {
         float acc[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = 0.f;
@@ -140,7 +145,8 @@ hipError_t moe_launch_combine(const void *out_perm, int out_f32, const int32_t *
                               const float *gw, const void *residual, int dt, int64_t T, int d,
                               int k, void *y, hipStream_t s) {
     using namespace moe;
-    const dim3 grid((unsigned)((T + kRowWaves - 1) / kRowWaves)), block(kRowWaves * kWave);
+    const int64_t waves = T * ((d + kCombinePiece - 1) / kCombinePiece);
+    const dim3 grid((unsigned)((waves + kRowWaves - 1) / kRowWaves)), block(kRowWaves * kWave);
     if (dt == 0)
         hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s,
                            (const float *)out_perm, row_of, gw, (const float *)residual, T, d, k,

@@ -72,12 +72,12 @@ constexpr int kRouterWaves = 4;
 // the sum over its tokens (in token order) of each expert's full softmax
 // probability (fp64, part_p[block][E]) and how many of its tokens' choices
 // went to each expert (part_c[block][E]).
-template <typename Tin, int TPW, int EG, int WPT, bool STATS = false>
-__global__ __launch_bounds__(kRouterWaves * kWave) void router_topk_kernel(
+template <typename Tin, int TPW, int EG, int WPT, bool STATS = false, int WAVES = kRouterWaves>
+__global__ __launch_bounds__(WAVES * kWave) void router_topk_kernel(
     const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,
     int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits,
     double *__restrict__ part_p = nullptr, int32_t *__restrict__ part_c = nullptr) {
-    constexpr int kGroups = kRouterWaves / WPT;  // token groups per workgroup
+    constexpr int kGroups = WAVES / WPT;  // token groups per workgroup
     __shared__ float s_logit[kGroups][TPW][64];
     __shared__ double s_part[kGroups][WPT][TPW * EG];
     __shared__ double s_prob[STATS ? kGroups * TPW : 1][64];
@@ -273,7 +273,19 @@ hipError_t launch_router_impl(const void *x, int dt, const float *Wg, int64_t T,
     using namespace moe;
     const dim3 block(kRouterWaves * kWave);
     const dim3 grid((unsigned)moe_router_blocks(T));
-    if (router_wide_rows(T)) {
+    if (T <= 256 && d % (16 * 8) == 0) {
+        // decode sizes: sixteen waves split each token's row, so the few
+        // tokens still spread over the chip
+        const dim3 block16(16 * kWave);
+        if (dt == 0)
+            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 16, STATS, 16>), grid, block16, 0,
+                               s, (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p,
+                               part_c);
+        else
+            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 16, STATS, 16>), grid, block16,
+                               0, s, (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, part_p,
+                               part_c);
+    } else if (router_wide_rows(T)) {
         if (dt == 0)
             hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 4, STATS>), grid, block, 0, s,
                                (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p, part_c);
