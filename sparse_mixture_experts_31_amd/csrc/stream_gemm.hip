@@ -51,6 +51,7 @@ constexpr int kSWStage = kSGrp * 1024;
 constexpr int kSTokBuf = kSBT * 1024;
 constexpr int kSMapMax = 33 * 64;  // token_of entries: A < 33 E on this path, E <= 64
 constexpr int kSLds = kSP * kSWStage + 2 * kSTokBuf + kSMapMax * 4;
+constexpr int kSPartHdr = 64;  // floats before the chunk slices (the chosen chunk count)
 static_assert(kSLds <= 160 * 1024 - 1024, "LDS capacity");
 static_assert(kSGrp == 16 && kSGroups == 8, "one 16-row MFMA fragment per stage, 8 per K range");
 static_assert(kSP - 1 <= kSGroups / 2, "prologue stages carry no token loads");
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ gather,
     const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb,
     const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out,
-    int kc, float *__restrict__ part) {
+    int kc_max, float *__restrict__ part) {
     constexpr int P = kSP, G = kSGroups;
     constexpr int kCols = SWIGLU ? kSRowsT / 2 : kSRowsT;  // output columns per tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -111,11 +112,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = tid; i < A; i += 256) s_map[i] = gather[i];
     __syncthreads();
     auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-    // Work items: tile t's K ranges cut into kc contiguous chunks (kc > 1
-    // only for GEMM2 at the smallest batches, where whole tiles would leave
-    // CUs idle); item w = kc t + chunk, taken round robin.
-    const int total = u(s_first[E]) * kc;
+    // Work items: tile t's K ranges cut into kc contiguous chunks; item
+    // w = kc t + chunk, taken round robin.  With few tiles (small batches)
+    // whole tiles leave CUs idle for much of the kernel: kc is then the
+    // count in 1, 2, 4 (<= kc_max and the K ranges) that finishes first in
+    // units of whole tiles, ceil(tiles kc / grid) / kc, taking a larger
+    // count only for a gain of 5 % or more (shorter chunks stream each
+    // weight row in fewer, shorter runs) -- the same choice in every
+    // workgroup, recorded for stream_reduce_kernel.
     const int NG = gridDim.x;
+    const int tiles = u(s_first[E]);
+    int kc = 1;
+    for (int c = 2; c <= kc_max && c <= n_kr; c *= 2)
+        if (20 * (int64_t)((tiles * c + NG - 1) / NG) * kc <
+            19 * (int64_t)((tiles * kc + NG - 1) / NG) * c)
+            kc = c;
+    if (kc_max > 1 && blockIdx.x == 0 && tid == 0) *(int *)part = kc;
+    float *const slices = part + kSPartHdr;
+    const int total = tiles * kc;
     const int my_items = (total > (int)blockIdx.x) ? (total - (int)blockIdx.x + NG - 1) / NG : 0;
     if (my_items == 0) return;  // uniform over the workgroup
 
@@ -299,8 +313,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // (h = 0..3) for tokens 16 jfrag .. + 16: lane l has weight rows
         // 4 (l / 16) .. + 4 of a group, for token l % 16.  GEMM1: groups
         // par, par + 2 are W1 rows, par + 4, par + 6 the same W3 rows.  A
-        // K chunk of a tile (kc > 1, GEMM2) leaves its fp32 sums in its slice
-        // of `part` for stream_reduce_kernel.
+        // K chunk of a tile (kc > 1) leaves its raw fp32 sums in its slice
+        // of `part` for stream_reduce_kernel (GEMM1: u at column n, v at
+        // column N + n of a 2N-wide row).
         const int m = 16 * jfrag + lr;
         if (m < cti.mrem) {
             const int64_t row = cti.row0 + m;
@@ -308,8 +323,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int h = 0; h < (SWIGLU ? 2 : 4); ++h) {
                 const int n = cti.n0 + 16 * (par + 2 * h) + 4 * lq;
                 if (n < N) {
-                    if (!SWIGLU && kc > 1) {
-                        *(f32x4 *)(part + ((int64_t)cit.chunk * A + row) * N + n) = acc[h];
+                    if (kc > 1) {
+                        constexpr int W = SWIGLU ? 2 : 1;
+                        float *sl = slices + ((int64_t)cit.chunk * A + row) * (W * N);
+                        *(f32x4 *)(sl + n) = acc[h];
+                        if constexpr (SWIGLU) *(f32x4 *)(sl + N + n) = acc[h + 2];
                     } else {
                         float r[4];
 #pragma unroll
@@ -328,61 +346,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_vmcnt_lgkm0<0>();  // the trailing reloads land before the wave ends
 }
 
-// out[i] = sum over the kc slices of part[s][i], in slice order (the K
-// chunks of a GEMM2 tile, so the sum is the same on every run).
-template <typename TO>
+// The K chunks' partial sums added in chunk order (so the sum is the same
+// on every run), then the epilogue: GEMM2 out[r][n] = sum_c o_c[r][n];
+// GEMM1 out[r][n] = silu(sum_c u_c[r][n]) * sum_c v_c[r][n].  Nothing to do
+// when the GEMM kernel chose one chunk.
+template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restrict__ part,
-                                                            int kc, int64_t n4,
+                                                            int64_t A, int N,
                                                             TO *__restrict__ out) {
+    const int kc = *(const int *)part;
+    if (kc <= 1) return;
+    const float *slices = part + kSPartHdr;
+    constexpr int W = SWIGLU ? 2 : 1;
+    const int64_t n4 = A * N / 4;               // N is a multiple of 512
+    const int64_t slice = A * (int64_t)(W * N);  // floats per chunk
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
          i += (int64_t)gridDim.x * 256) {
-        f32x4 r = ((const f32x4 *)part)[i];
-        for (int c = 1; c < kc; ++c) r += ((const f32x4 *)part)[c * n4 + i];
-        store4<TO>(out + 4 * i, r[0], r[1], r[2], r[3]);
+        const int64_t r = (4 * i) / N, n = (4 * i) % N;
+        const float *p = slices + r * (W * N) + n;
+        f32x4 uu = *(const f32x4 *)p, vv = {};
+        if constexpr (SWIGLU) vv = *(const f32x4 *)(p + N);
+        for (int c = 1; c < kc; ++c) {
+            uu += *(const f32x4 *)(p + c * slice);
+            if constexpr (SWIGLU) vv += *(const f32x4 *)(p + c * slice + N);
+        }
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = SWIGLU ? silu(uu[q]) * vv[q] : uu[q];
+        store4<TO>(out + 4 * i, o[0], o[1], o[2], o[3]);
     }
 }
 
 namespace {
 
-// K chunks per GEMM2 tile: at the smallest batches (fewer than two rows per
-// expert on average) the GEMM2 tiles, at most min(E, A) experts x ceil(d /
-// 128), leave CUs idle; cutting each tile's K ranges into chunks gives
-// every CU about two items.  Otherwise 1.
-int stream_chunks(int64_t A, int d, int d_ff, int E) {
-    if (A <= 0 || A >= 2 * (int64_t)E) return 1;
-    const int64_t tiles = std::min<int64_t>(E, A) * ((d + kSRowsT - 1) / kSRowsT);
-    if (tiles <= 0) return 1;
-    const int64_t kc = (2 * (int64_t)device_cus() + tiles - 1) / tiles;
-    return (int)std::max<int64_t>(1, std::min<int64_t>(kc, d_ff / kSKRange));
-}
+// Most K chunks a launch may cut its tiles into: only at the smallest
+// batches (fewer than four rows per expert on average), where the tile count
+// can leave CUs idle.  The kernel picks the count it uses.
+int stream_chunk_limit(int64_t A, int E) { return (A > 0 && A < 4 * (int64_t)E) ? 4 : 1; }
 
 template <bool SWIGLU, typename TO>
 hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
-                         void *out, int kc, float *part, hipStream_t s) {
+                         void *out, int kc_max, float *part, hipStream_t s) {
     hipError_t err = set_lds_limit<stream_gemm_kernel<SWIGLU, TO>>(kSLds);
     if (err != hipSuccess) return err;
-    // one workgroup per CU, never more than there are items:
-    // sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1 tiles, kc items each
+    // one workgroup per CU, never more than there can be items:
+    // sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1 tiles, kc_max items each
     const int64_t cols = SWIGLU ? kSRowsT / 2 : kSRowsT;
-    const int64_t item_bound = (N + cols - 1) / cols * ((A + kSBT - 1) / kSBT + E - 1) * kc;
+    const int64_t item_bound = (N + cols - 1) / cols * ((A + kSBT - 1) / kSBT + E - 1) * kc_max;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), item_bound));
     hipLaunchKernelGGL((stream_gemm_kernel<SWIGLU, TO>), dim3(grid), dim3(256), kSLds, s,
                        (const bf16_t *)act, act_ld, gather, (const bf16_t *)Wa,
-                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, kc, part);
-    if ((err = hipGetLastError()) != hipSuccess || kc == 1) return err;
+                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, kc_max, part);
+    if ((err = hipGetLastError()) != hipSuccess || kc_max == 1) return err;
     const int64_t n4 = A * N / 4;  // N is a multiple of 512
     const int rgrid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
-    hipLaunchKernelGGL((stream_reduce_kernel<TO>), dim3(rgrid), dim3(256), 0, s,
-                       (const float *)part, kc, n4, (TO *)out);
+    hipLaunchKernelGGL((stream_reduce_kernel<SWIGLU, TO>), dim3(rgrid), dim3(256), 0, s,
+                       (const float *)part, A, N, (TO *)out);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t stream_partial_bytes(int64_t A, int d, int d_ff, int E) {
-    const int kc = stream_chunks(A, d, d_ff, E);
-    return kc > 1 ? (size_t)kc * A * d * sizeof(float) : 0;
+    // header + the larger of GEMM1's (u and v: 2 d_ff per row) and GEMM2's
+    // (d per row) chunk slices; the two launches run one after the other
+    const int kc = stream_chunk_limit(A, E);
+    if (kc == 1) return 0;
+    return sizeof(float) * ((size_t)kSPartHdr + (size_t)kc * A * std::max(2 * d_ff, d));
 }
 
 bool stream_supported(int64_t A, int d, int d_ff, int E) {
@@ -396,13 +427,13 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
                              int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
                              float *partial, size_t partial_bytes, hipEvent_t mid,
                              hipStream_t s) {
+    // K chunks only when the scratch for their partial sums is there
+    int kc = stream_chunk_limit(A, E);
+    if (kc > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) kc = 1;
     hipError_t err = launch_stream<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A,
-                                                 hbuf, 1, nullptr, s);
+                                                 hbuf, kc, partial, s);
     if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
     if (err != hipSuccess) return err;
-    // GEMM2 in K chunks when the scratch for their partial sums is there
-    int kc = stream_chunks(A, d, d_ff, E);
-    if (kc > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) kc = 1;
     if (out_f32)
         return launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff,
                                            A, out, kc, partial, s);
