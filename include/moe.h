@@ -129,9 +129,10 @@ moe_status moe_permute(const void *x, const int32_t *topk_idx, moe_dtype dt, int
  * x_perm, out_perm [T*k][d] (dt); offsets int32 [E+1] on the device (as
  * produced by moe_permute; offsets[E] <= T*k).  Rows at or beyond offsets[E]
  * are left untouched.  ws holds the SwiGLU intermediate (rows x d_ff) and,
- * for large bf16 batches, fp32 partial sums of tiles split along K (summed
- * in a fixed order: results are deterministic); moe_workspace_size() bytes
- * always suffice.
+ * for large bf16 batches and for the smallest ones (fewer than four rows per
+ * expert), fp32 partial sums of tiles split along K (summed in a fixed
+ * order: results are deterministic); moe_workspace_size() bytes always
+ * suffice.
  * Defined by: fdeinterviews breakdown, "The paper in one minute" (the experts
  * are SwiGLU blocks);
  * tokentrails lineage, Code listing (w2(silu(w1(x)) * w3(x))). */
