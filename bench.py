@@ -184,8 +184,11 @@ def decode_sweep(w, L, moe, np, torch, stream, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the first few dozen layers of a fresh process run slower (decode: 0.52 ms
+    # for the first ten, 0.45 from about the thirtieth on), so the default
+    # warm-up covers them
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "prefill", "skewed", "stack"])
     ap.add_argument("--seed", type=int, default=0)

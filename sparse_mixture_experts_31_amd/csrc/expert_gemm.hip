@@ -91,20 +91,7 @@ __global__ __launch_bounds__(WN *WM *kWave) void grouped_gemm_kernel(
     const int wave = tid / kWave;
     const int n_tiles = (N + C::kCols - 1) / C::kCols;
 
-    // Offsets are clamped to [0, A] so that no row index leaves the buffers
-    // even for a malformed offsets array.
-    if (tid == 0) {
-        int first = 0;
-        for (int i = 0; i < E; ++i) {
-            const int lo = min(max(offsets[i], 0), A);
-            const int hi = min(max(offsets[i + 1], lo), A);
-            s_lo[i] = lo;
-            s_cnt[i] = hi - lo;
-            s_first[i] = first;
-            first += (hi - lo + BT - 1) / BT * n_tiles;
-        }
-        s_first[E] = first;
-    }
+    if (wave == 0) build_expert_table(offsets, E, A, BT, n_tiles, s_lo, s_cnt, s_first);
     __syncthreads();
     const int total = s_first[E];
 

@@ -53,6 +53,37 @@ __device__ __forceinline__ f32x4 mma16(i32x4 a, i32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// The grouped GEMMs' per-expert table, built by one whole wave (E <= 64):
+// lo[i] = expert i's first row, cnt[i] = its rows, first[i] = the tiles of
+// the experts before it (first[E] = all tiles), for token tiles of `bt` rows
+// times `col_tiles` column tiles.  Every lane loads its two offsets at once
+// and a shuffle scan adds the tile counts, so the table costs one memory
+// round trip instead of one per expert.  Offsets are clamped to [0, A] so no
+// row index leaves the buffers even for a malformed offsets array.  The
+// caller syncs the workgroup before the table is read.
+__device__ __forceinline__ void build_expert_table(const int32_t *__restrict__ offsets, int E,
+                                                   int A, int bt, int col_tiles, int *lo,
+                                                   int *cnt, int *first) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int o0 = lane < E ? offsets[lane] : 0;
+    const int o1 = lane < E ? offsets[lane + 1] : 0;
+    const int l = min(max(o0, 0), A);
+    const int h = min(max(o1, l), A);
+    const int tiles = lane < E ? (h - l + bt - 1) / bt * col_tiles : 0;
+    int incl = tiles;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    if (lane < E) {
+        lo[lane] = l;
+        cnt[lane] = h - l;
+        first[lane] = incl - tiles;
+    }
+    if (lane == E - 1) first[E] = incl;
+}
+
 template <typename T>
 __device__ __forceinline__ void store4(T *out, float v0, float v1, float v2, float v3);
 

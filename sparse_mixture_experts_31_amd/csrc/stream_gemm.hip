@@ -94,22 +94,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int col_tiles = (N + kCols - 1) / kCols;
     const int n_kr = K / kSKRange;  // >= 1, checked by the launcher
 
-    // Per-expert tile table (token tiles fastest, then column tiles); offsets
-    // clamped to [0, A] so no row index leaves the buffers.
-    if (tid == 0) {
-        int f = 0;
-        for (int i = 0; i < E; ++i) {
-            const int lo = min(max(offsets[i], 0), A);
-            const int hi = min(max(offsets[i + 1], lo), A);
-            s_lo[i] = lo;
-            s_cnt[i] = hi - lo;
-            s_first[i] = f;
-            f += (hi - lo + kSBT - 1) / kSBT * col_tiles;
+    // Per-expert tile table (token tiles fastest, then column tiles) by wave
+    // 0; meanwhile the other three copy the token map, four loads in flight
+    // per lane, so the whole set-up is about one memory round trip.
+    if (wave == 0) {
+        build_expert_table(offsets, E, A, kSBT, col_tiles, s_lo, s_cnt, s_first);
+    } else if (gather) {
+        constexpr int kStride = 256 - kWave;
+        for (int i0 = tid - kWave; i0 < A; i0 += 4 * kStride) {
+            int v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = i0 + q * kStride < A ? gather[i0 + q * kStride] : 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (i0 + q * kStride < A) s_map[i0 + q * kStride] = v[q];
         }
-        s_first[E] = f;
     }
-    if (gather)
-        for (int i = tid; i < A; i += 256) s_map[i] = gather[i];
     __syncthreads();
     auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
     // Work items: tile t's K ranges cut into kc contiguous chunks; item

@@ -68,19 +68,9 @@ __device__ __forceinline__ int swz128(int r, int c) {
 struct TileTable {
     int *lo, *cnt, *first;
     int E;
-    // Offsets are clamped to [0, A] so no row index leaves the buffers even
-    // for a malformed offsets array.  Called by one thread; the caller syncs.
+    // Called by one whole wave; the caller syncs.
     __device__ void build(const int32_t *offsets, int A, int col_tiles) {
-        int f = 0;
-        for (int i = 0; i < E; ++i) {
-            const int l = min(max(offsets[i], 0), A);
-            const int h = min(max(offsets[i + 1], l), A);
-            lo[i] = l;
-            cnt[i] = h - l;
-            first[i] = f;
-            f += (h - l + kWideBT - 1) / kWideBT * col_tiles;
-        }
-        first[E] = f;
+        build_expert_table(offsets, E, A, kWideBT, col_tiles, lo, cnt, first);
     }
     // The table is the same for every lane: reading it through
     // readfirstlane keeps the tile and segment arithmetic in scalar
@@ -189,7 +179,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int n_k = K / kWideKStep;  // >= P, checked by the launcher
 
     TileTable tt{s_lo, s_cnt, s_first, E};
-    if (tid == 0) tt.build(offsets, A, (N + kCols - 1) / kCols);
+    if (wave == 0) tt.build(offsets, A, (N + kCols - 1) / kCols);
     __syncthreads();
 
     const int G8 = gridDim.x / 8;  // workgroups per XCD (grid is a multiple of 8)
@@ -466,8 +456,9 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
     TileTable tt{s_lo, s_cnt, s_first, E};
     const int frag = blockIdx.x % 16, xcd = (blockIdx.x / 16) % 8, jr = blockIdx.x / 128;
     if (SWIGLU && frag >= 8) return;
+    if (tid < kWave) tt.build(offsets, A, (N + kCols - 1) / kCols);
+    __syncthreads();
     if (tid == 0) {
-        tt.build(offsets, A, (N + kCols - 1) / kCols);
         const XcdShare xs(tt.total(), xcd, G8, n_k, n_k % kWideP == 0);
         int np = 0;
         if (xs.split && jr < xs.left) {
