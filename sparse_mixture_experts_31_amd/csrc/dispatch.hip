@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_index_kernel(
         int rank = 0;
         while (rem) {
             const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int le = __shfl(e, leader);
+            const int le = __builtin_amdgcn_readlane(e, leader);  // leader is wave-uniform
             const uint64_t m = __ballot(e == le);
             if (e == le) rank = __popcll(m & lower_lanes);
             if (lane == leader) s_wave[wave][le] = __popcll(m);

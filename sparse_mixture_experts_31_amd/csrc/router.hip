@@ -18,7 +18,7 @@
 // then picks the top k of token t (strict '>' over ascending expert index, so
 // equal fp32 scores go to the lower index) and the gates
 // g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
-#include "common.h"
+#include "gemm_common.h"
 
 namespace moe {
 
@@ -66,6 +66,51 @@ __device__ __forceinline__ void wave_reduce_halving(double (&v)[NV], int lane) {
 
 constexpr int kRouterWaves = 4;
 
+// The top k of E fp32 scores L (strict '>' over ascending expert index, so
+// equal scores go to the lower index): sel[j], sl[j] for j < k.
+__device__ __forceinline__ void select_topk(const float *L, int E, int k, int (&sel)[8],
+                                            float (&sl)[8]) {
+    uint64_t used = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        sel[j] = 0;
+        sl[j] = 0.f;
+        if (j < k) {
+            int best = -1;
+            float bv = 0.f;
+            for (int e = 0; e < E; ++e) {
+                if ((used >> e) & 1ull) continue;
+                const float v = L[e];
+                if (best < 0 || v > bv) {
+                    best = e;
+                    bv = v;
+                }
+            }
+            used |= 1ull << best;
+            sel[j] = best;
+            sl[j] = bv;
+        }
+    }
+}
+
+// Token t's choices and gates g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+__device__ __forceinline__ void write_choice(int64_t t, int k, const int (&sel)[8],
+                                             const float (&sl)[8], int32_t *__restrict__ out_idx,
+                                             float *__restrict__ out_w) {
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < k) z += expf(sl[j] - sl[0]);
+    const int64_t o = t * k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j < k) {
+            out_idx[o + j] = sel[j];
+            out_w[o + j] = expf(sl[j] - sl[0]) / z;
+        }
+    }
+}
+
 // WPT waves share each group of TPW tokens, every wave covering a contiguous
 // 1/WPT of d; their fp64 partial sums meet in LDS and are added in wave order.
 // With STATS the workgroup also leaves, for the load-balancing statistics,
@@ -94,28 +139,32 @@ __global__ __launch_bounds__(WAVES * kWave) void router_topk_kernel(
         double acc[TPW * EG];
 #pragma unroll
         for (int i = 0; i < TPW * EG; ++i) acc[i] = 0.0;
+#pragma unroll 1
         for (int i = dlo + lane * 8; i < dhi; i += kWave * 8) {
             float xv[TPW][8];
+            // rows past T and experts past E are clamped to valid ones (no
+            // branches, so the conversions stay next to their use); their
+            // sums are never stored
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                if (tok0 + t < T) {
-                    load8<Tin>(x + (tok0 + t) * (int64_t)d + i, xv[t]);
-                } else {
+            for (int t = 0; t < TPW; ++t)
+                load8<Tin>(x + min(tok0 + t, T - 1) * (int64_t)d + i, xv[t]);
+            // all EG experts' weights first, then the products with the
+            // experts innermost: EG independent accumulation chains in flight
+            // (each accumulator still takes its 8 products in order)
+            float wv[EG][8];
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) xv[t][c] = 0.f;
-                }
-            }
+            for (int j = 0; j < EG; ++j)
+                load8<float>(Wg + (int64_t)min(e0 + j, E - 1) * d + i, wv[j]);
 #pragma unroll
-            for (int j = 0; j < EG; ++j) {
-                if (e0 + j < E) {
-                    float wv[8];
-                    load8<float>(Wg + (int64_t)(e0 + j) * d + i, wv);
+            for (int c = 0; c < 8; ++c) {
 #pragma unroll
-                    for (int t = 0; t < TPW; ++t)
+                for (int t = 0; t < TPW; ++t)
 #pragma unroll
-                        for (int c = 0; c < 8; ++c)
-                            acc[t * EG + j] = fma((double)xv[t][c], (double)wv[c], acc[t * EG + j]);
-                }
+                    for (int j = 0; j < EG; ++j)
+                        acc[t * EG + j] = fma((double)xv[t][c], (double)wv[j][c], acc[t * EG + j]);
+                // one element's conversions at a time (else they are all
+                // hoisted and the registers run out)
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         wave_reduce_halving<TPW * EG>(acc, lane);
@@ -143,43 +192,10 @@ __global__ __launch_bounds__(WAVES * kWave) void router_topk_kernel(
             const int t = lane;
             const bool valid = tok0 + t < T;
             const float *L = s_logit[grp][t];
-            uint64_t used = 0;
             int sel[8];
             float sl[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                sel[j] = 0;
-                sl[j] = 0.f;
-                if (j < k) {
-                    int best = -1;
-                    float bv = 0.f;
-                    for (int e = 0; e < E; ++e) {
-                        if ((used >> e) & 1ull) continue;
-                        const float v = L[e];
-                        if (best < 0 || v > bv) {
-                            best = e;
-                            bv = v;
-                        }
-                    }
-                    used |= 1ull << best;
-                    sel[j] = best;
-                    sl[j] = bv;
-                }
-            }
-            if (valid) {
-                float z = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (j < k) z += expf(sl[j] - sl[0]);
-                const int64_t o = (tok0 + t) * k;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if (j < k) {
-                        out_idx[o + j] = sel[j];
-                        out_w[o + j] = expf(sl[j] - sl[0]) / z;
-                    }
-                }
-            }
+            select_topk(L, E, k, sel, sl);
+            if (valid) write_choice(tok0 + t, k, sel, sl, out_idx, out_w);
             if constexpr (STATS) {
                 // full softmax over all E scores (l_max = sl[0]), in fp64
                 const int slot = grp * TPW + t;
@@ -205,6 +221,83 @@ __global__ __launch_bounds__(WAVES * kWave) void router_topk_kernel(
             }
             part_p[(int64_t)blockIdx.x * E + e] = p;
             part_c[(int64_t)blockIdx.x * E + e] = c;
+        }
+    }
+}
+
+constexpr int kRouterLdsWaves = 8;
+constexpr int kRouterLdsBytes = 128 * 1024;  // most Wg bytes held in LDS
+
+// Many tokens: every wave of router_topk_kernel's one-wave-per-token form
+// reads all of Wg (E d fp32) per token, which at thousands of tokens makes
+// the router an L2 stream of T times Wg.  Here a workgroup copies Wg into
+// LDS once and its eight waves walk tokens (wave w of workgroup b: tokens
+// 8 b + w, then a grid further).  A lane covers the same elements of d in
+// the same order with the same fp64 steps and the same wave reduction as in
+// router_topk_kernel, so the scores are the same bit for bit; the token's
+// row is fetched eight pieces at a time so its loads are in flight together.
+template <typename Tin, int Q>
+__global__ __launch_bounds__(kRouterLdsWaves * kWave) void router_topk_lds_kernel(
+    const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,
+    int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits) {
+    extern __shared__ __attribute__((aligned(16))) float s_wg[];  // [E][d]
+    __shared__ float s_logit[kRouterLdsWaves][64];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    // Wg into LDS, sixteen 16-byte loads in flight per thread
+    const int n4 = E * d / 4;  // d is a multiple of 8
+    constexpr int kThreads = kRouterLdsWaves * kWave, kBatch = 16;
+    for (int i0 = threadIdx.x; i0 < n4; i0 += kBatch * kThreads) {
+        float4 v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)  // clamped, so the loads need no branch
+            v[q] = ((const float4 *)Wg)[min(i0 + q * kThreads, n4 - 1)];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (i0 + q * kThreads < n4) ((float4 *)s_wg)[i0 + q * kThreads] = v[q];
+    }
+    __syncthreads();
+
+    constexpr int kStep = kWave * 8;  // elements of d per lane step
+    for (int64_t t = (int64_t)blockIdx.x * kRouterLdsWaves + wave; t < T;
+         t += (int64_t)gridDim.x * kRouterLdsWaves) {
+        const Tin *xr = x + t * (int64_t)d;
+        for (int e0 = 0; e0 < E; e0 += 8) {
+            double acc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+            // d is a multiple of Q kStep: Q pieces of the row per batch
+#pragma unroll 1
+            for (int i0 = lane * 8; i0 < d; i0 += Q * kStep) {
+                float xv[Q][8];
+#pragma unroll
+                for (int q = 0; q < Q; ++q) load8<Tin>(xr + i0 + q * kStep, xv[q]);
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    // experts innermost: eight independent chains (experts
+                    // past E read a valid row; their sums are never stored)
+                    float wv[8][8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        load8<float>(s_wg + min(e0 + j, E - 1) * d + i0 + q * kStep, wv[j]);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            acc[j] = fma((double)xv[q][c], (double)wv[j][c], acc[j]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+            wave_reduce_halving<8>(acc, lane);
+            if ((lane & 7) == 0 && e0 + lane / 8 < E) s_logit[wave][e0 + lane / 8] = (float)acc[0];
+        }
+        if (out_logits && lane < E) out_logits[t * E + lane] = s_logit[wave][lane];
+        if (lane == 0) {
+            int sel[8];
+            float sl[8];
+            select_topk(s_logit[wave], E, k, sel, sl);
+            write_choice(t, k, sel, sl, out_idx, out_w);
         }
     }
 }
@@ -266,6 +359,32 @@ namespace {
 // wave at T = 4096; 7.7 us against 16.7 us the other way at T = 32).
 bool router_wide_rows(int64_t T) { return T < 1024; }
 
+template <typename Tin, int Q>
+hipError_t launch_router_lds_q(const Tin *x, const float *Wg, int64_t T, int d, int E, int k,
+                               int32_t *idx, float *gw, float *logits, hipStream_t s) {
+    using namespace moe;
+    const int bytes = E * d * (int)sizeof(float);  // <= kRouterLdsBytes
+    hipError_t err = set_lds_limit<router_topk_lds_kernel<Tin, Q>>(kRouterLdsBytes);
+    if (err != hipSuccess) return err;
+    const int64_t blocks =
+        std::min<int64_t>(device_cus(), (T + kRouterLdsWaves - 1) / kRouterLdsWaves);
+    hipLaunchKernelGGL((router_topk_lds_kernel<Tin, Q>), dim3((unsigned)blocks),
+                       dim3(kRouterLdsWaves * kWave), bytes, s, x, Wg, T, d, E, k, idx, gw,
+                       logits);
+    return hipGetLastError();
+}
+
+// Row pieces per batch: the most of 8, 4, 2, 1 that divides d / 512.
+template <typename Tin>
+hipError_t launch_router_lds(const Tin *x, const float *Wg, int64_t T, int d, int E, int k,
+                             int32_t *idx, float *gw, float *logits, hipStream_t s) {
+    const int n = d / 512;
+    if (n % 8 == 0) return launch_router_lds_q<Tin, 8>(x, Wg, T, d, E, k, idx, gw, logits, s);
+    if (n % 4 == 0) return launch_router_lds_q<Tin, 4>(x, Wg, T, d, E, k, idx, gw, logits, s);
+    if (n % 2 == 0) return launch_router_lds_q<Tin, 2>(x, Wg, T, d, E, k, idx, gw, logits, s);
+    return launch_router_lds_q<Tin, 1>(x, Wg, T, d, E, k, idx, gw, logits, s);
+}
+
 template <bool STATS>
 hipError_t launch_router_impl(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
                               int k, int32_t *idx, float *gw, float *logits, double *part_p,
@@ -273,6 +392,11 @@ hipError_t launch_router_impl(const void *x, int dt, const float *Wg, int64_t T,
     using namespace moe;
     const dim3 block(kRouterWaves * kWave);
     const dim3 grid((unsigned)moe_router_blocks(T));
+    if (!STATS && !router_wide_rows(T) && d % 512 == 0 && (int64_t)E * d * 4 <= kRouterLdsBytes) {
+        // many tokens, Wg small enough for LDS
+        if (dt == 0) return launch_router_lds((const float *)x, Wg, T, d, E, k, idx, gw, logits, s);
+        return launch_router_lds((const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, s);
+    }
     if (T <= 256 && d % (16 * 8) == 0) {
         // decode sizes: sixteen waves split each token's row, so the few
         // tokens still spread over the chip

@@ -94,8 +94,13 @@ def test_layer_error_is_the_output_rounding(name):
     log(f"  normwise {err:.3e} against a one-rounding floor of {floor:.3e}")
 
 
-def test_route_scores_are_rounded_exact_dot_products():
-    w = Workload("mid-bf16", 10, T=300, d=512, d_ff=1024)
+@pytest.mark.parametrize("w", [
+    Workload("mid-bf16", 10, T=300, d=512, d_ff=1024),
+    # from 1024 tokens on, Wg sits in LDS and each wave walks tokens
+    Workload("many-bf16", 24, T=1100, d=512, d_ff=512),
+    Workload("many-f32-e13", 25, T=1030, d=512, d_ff=256, E=13, k=3, dtype="f32"),
+], ids=lambda w: w.name)
+def test_route_scores_are_rounded_exact_dot_products(w):
     L = _case(w)
     T, E = w.T, w.E
     logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
