@@ -114,19 +114,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
     // Work items: tile t's K ranges cut into kc contiguous chunks; item
     // w = kc t + chunk, taken round robin.  With few tiles (small batches)
-    // whole tiles leave CUs idle for much of the kernel: kc is then the
-    // count in 1, 2, 4 (<= kc_max and the K ranges) that finishes first in
-    // units of whole tiles, ceil(tiles kc / grid) / kc, taking a larger
-    // count only for a gain of 5 % or more (shorter chunks stream each
-    // weight row in fewer, shorter runs) -- the same choice in every
-    // workgroup, recorded for stream_reduce_kernel.
+    // whole tiles leave CUs idle for much of the kernel: kc is then 4 when
+    // that finishes at least 10 % sooner in units of whole tiles,
+    // ceil(4 tiles / grid) / 4 against ceil(tiles / grid), else 1.  (Two
+    // chunks measured slower than both one and four on MI355X -- by 10 %
+    // at T = 8, where the count predicted a 7 % gain -- and the chunks'
+    // partial sums and extra pass cost a few percent, hence the margin.)
+    // The same choice in every workgroup, recorded for stream_reduce_kernel.
     const int NG = gridDim.x;
     const int tiles = u(s_first[E]);
     int kc = 1;
-    for (int c = 2; c <= kc_max && c <= n_kr; c *= 2)
-        if (20 * (int64_t)((tiles * c + NG - 1) / NG) * kc <
-            19 * (int64_t)((tiles * kc + NG - 1) / NG) * c)
-            kc = c;
+    if (kc_max >= 4 && n_kr >= 4 &&
+        10 * (int64_t)((tiles * 4 + NG - 1) / NG) < 36 * (int64_t)((tiles + NG - 1) / NG))
+        kc = 4;
     if (kc_max > 1 && blockIdx.x == 0 && tid == 0) *(int *)part = kc;
     float *const slices = part + kSPartHdr;
     const int total = tiles * kc;
