@@ -10,12 +10,13 @@
 //   1. per-expert histogram with LDS integer atomics (order-free, exact);
 //   2. exclusive scan of the E counts -> offsets;
 //   3. stable ranks, 1024 assignments per round: inside a wave the lanes that
-//      share an expert are found with ballots (one ballot per distinct expert
-//      present in the wave), a lane's rank is the popcount of the matching
-//      lower lanes, and per-wave totals are prefix-summed across the 16 waves
-//      and carried into the next round.  Rows inside an expert's block thus
-//      follow ascending assignment index (t*k + j): a unique, deterministic
-//      order.
+//      share an expert are found with ballots (one per expert), a lane's rank
+//      is the popcount of the matching lower lanes, and per-wave totals are
+//      prefix-summed across the 16 waves and carried into the next round.
+//      The indices are staged in LDS 8192 at a time (eight loads in flight
+//      per thread), so a window costs one memory round trip instead of one
+//      per round.  Rows inside an expert's block thus follow ascending
+//      assignment index (t*k + j): a unique, deterministic order.
 // gather_rows_kernel: one wave per token reads the token's row once with
 //   16-byte loads and writes it to each of its k rows of x_perm.
 #include "common.h"
@@ -24,6 +25,18 @@ namespace moe {
 
 constexpr int kDispatchThreads = 1024;
 constexpr int kDispatchWaves = kDispatchThreads / kWave;
+constexpr int kDispatchWindow = 8192;  // indices staged in LDS at a time
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
+// every global store of the wave to complete, which here would stall each
+// round on the previous round's row_of / token_of stores; nothing in this
+// kernel reads those back.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS operations are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_index_kernel(
     const int32_t *__restrict__ idx, int A, int E, int k, int32_t *__restrict__ counts,
@@ -31,17 +44,35 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_index_kernel(
     __shared__ int s_cnt[64];
     __shared__ int s_base[64];
     __shared__ int s_wave[kDispatchWaves][64];
+    __shared__ int s_idx[kDispatchWindow];  // the assignments' experts, a window at a time
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
 
     if (tid < 64) s_cnt[tid] = 0;
-    __syncthreads();
-    for (int a = tid; a < A; a += kDispatchThreads) {
-        const int e = idx[a];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
+    lds_barrier();
+    // A window of the indices (kPer loads in flight per thread) into s_idx.
+    constexpr int kPer = kDispatchWindow / kDispatchThreads;
+    auto stage = [&](int w0) {
+        int v[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int a = w0 + q * kDispatchThreads + tid;
+            v[q] = (a < A) ? idx[a] : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) s_idx[q * kDispatchThreads + tid] = v[q];
+    };
+    // histogram, window by window (the first window stays staged)
+    for (int w0 = 0; w0 < A; w0 += kDispatchWindow) {
+        stage(w0);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int e = s_idx[q * kDispatchThreads + tid];  // this thread's own entry
+            if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
+        }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         int run = 0;
         for (int e = 0; e < E; ++e) {
@@ -52,36 +83,45 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_index_kernel(
         }
         offsets[E] = run;
     }
-    __syncthreads();
+    lds_barrier();
 
     const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int r0 = 0; r0 < A; r0 += kDispatchThreads) {
+        // a new window (the histogram left the last one staged); every
+        // thread reads only the entries it stored itself
+        if (r0 % kDispatchWindow == 0 && (r0 > 0 || A > kDispatchWindow)) stage(r0);
         const int a = r0 + tid;
-        const int e = (a < A) ? idx[a] : -1;
+        const int e = s_idx[r0 % kDispatchWindow + tid];
         const bool valid = (unsigned)e < (unsigned)E;
-        s_wave[wave][lane] = 0;
-        __syncthreads();
-        uint64_t rem = __ballot(valid);
-        int rank = 0;
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int le = __builtin_amdgcn_readlane(e, leader);  // leader is wave-uniform
-            const uint64_t m = __ballot(e == le);
-            if (e == le) rank = __popcll(m & lower_lanes);
-            if (lane == leader) s_wave[wave][le] = __popcll(m);
-            rem &= ~m;
+        // one ballot per expert (independent of each other, so they
+        // pipeline): a lane's rank among the lanes of its expert, and lane
+        // ex of the wave keeps expert ex's count
+        int rank = 0, cnt = 0;
+        for (int ex = 0; ex < E; ++ex) {
+            const uint64_t m = __ballot(e == ex);
+            if (e == ex) rank = __popcll(m & lower_lanes);
+            if (lane == ex) cnt = __popcll(m);
         }
-        __syncthreads();
-        if (tid < E) {
-            int run = s_base[tid];
-            for (int w = 0; w < kDispatchWaves; ++w) {
-                const int c = s_wave[w][tid];
-                s_wave[w][tid] = run;
-                run += c;
+        s_wave[wave][lane] = cnt;
+        lds_barrier();
+        // per expert, the waves' counts to first rows: thread 16 e + w holds
+        // wave w's count, and the 16 of an expert share a wave (a segmented
+        // shuffle scan instead of a loop over the waves)
+        static_assert(kDispatchWaves == 16, "one 16-lane segment per expert");
+        if (tid < kDispatchWaves * E) {
+            const int ex = tid / kDispatchWaves, w = tid % kDispatchWaves;
+            const int c = s_wave[w][ex];
+            int incl = c;
+#pragma unroll
+            for (int dd = 1; dd < kDispatchWaves; dd <<= 1) {
+                const int v = __shfl_up(incl, dd, kDispatchWaves);
+                if (w >= dd) incl += v;
             }
-            s_base[tid] = run;
+            const int base = s_base[ex];
+            s_wave[w][ex] = base + incl - c;
+            if (w == kDispatchWaves - 1) s_base[ex] = base + incl;
         }
-        __syncthreads();
+        lds_barrier();
         if (valid) {
             const int row = s_wave[wave][e] + rank;
             row_of[a] = row;
@@ -89,7 +129,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_index_kernel(
         } else if (a < A) {
             row_of[a] = -1;
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
