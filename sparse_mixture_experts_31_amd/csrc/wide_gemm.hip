@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
                                                          const float *__restrict__ partial) {
     constexpr int kCols = SWIGLU ? kWideBW / 2 : kWideBW;
     __shared__ int s_lo[64], s_cnt[64], s_first[65];
-    __shared__ int s_slots[64], s_nparts, s_tile;  // G8 <= 64: one part per workgroup at most
+    __shared__ int s_slots[64], s_nparts;  // G8 <= 64: one part per workgroup at most
     const int tid = threadIdx.x;
     const int n_k = K / kWideKStep;
     TileTable tt{s_lo, s_cnt, s_first, E};
@@ -458,30 +458,33 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
     if (SWIGLU && frag >= 8) return;
     if (tid < kWave) tt.build(offsets, A, (N + kCols - 1) / kCols);
     __syncthreads();
-    if (tid == 0) {
-        const XcdShare xs(tt.total(), xcd, G8, n_k, n_k % kWideP == 0);
-        int np = 0;
-        if (xs.split && jr < xs.left) {
-            const int t_lo = jr * n_k, t_hi = t_lo + n_k;
-            for (int w = 0; w < G8 && np >= 0; ++w) {
-                const int b_lo = xs.bound(w, G8), b_hi = xs.bound(w + 1, G8);
-                if (b_hi <= t_lo || b_lo >= t_hi || b_hi <= b_lo) continue;
-                if (b_lo <= t_lo && b_hi >= t_hi) {
-                    np = -1;  // one workgroup did the whole tile and stored it
-                    break;
-                }
-                // its first split tile went to slot 0, a later one to slot 1
-                s_slots[np++] = (w * 8 + xcd) * 2 + (jr == b_lo / n_k ? 0 : 1);
-            }
-            s_tile = xs.lo + xs.rounds * G8 + jr;
+    const XcdShare xs(tt.total(), xcd, G8, n_k, n_k % kWideP == 0);
+    if (!xs.split || jr >= xs.left) return;  // uniform over the workgroup
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    if (wave == 0) {
+        // lane w < G8: does workgroup w's share of the split stages cover
+        // this tile in part (a partial in one of its slots) or whole (it
+        // stored the tile itself)?  Parts are taken in workgroup order.
+        const int t_lo = jr * n_k, t_hi = t_lo + n_k;
+        bool part = false, whole = false;
+        int slot = 0;
+        if (lane < G8) {
+            const int b_lo = xs.bound(lane, G8), b_hi = xs.bound(lane + 1, G8);
+            const bool overlap = !(b_hi <= t_lo || b_lo >= t_hi || b_hi <= b_lo);
+            whole = overlap && b_lo <= t_lo && b_hi >= t_hi;
+            part = overlap && !whole;
+            // its first split tile went to slot 0, a later one to slot 1
+            slot = (lane * 8 + xcd) * 2 + (jr == b_lo / n_k ? 0 : 1);
         }
-        s_nparts = np;
+        const uint64_t wm = __ballot(whole), pm = __ballot(part);
+        const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        if (part && !wm) s_slots[__popcll(pm & lower_lanes)] = slot;
+        if (lane == 0) s_nparts = wm ? -1 : __popcll(pm);
     }
     __syncthreads();
     const int np = s_nparts;
     if (np <= 0) return;
-    const TileInfo ti = tt.info(s_tile, kCols);
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const TileInfo ti = tt.info(xs.lo + xs.rounds * G8 + jr, kCols);
     const int wn = wave & 1, wm = wave >> 1;
     auto load_sum = [&](int p) {
         f32x4 r{};
