@@ -289,12 +289,23 @@ static hipError_t launch_grouped(const void *act, int64_t act_ld, const void *Wa
 // (wide_gemm.hip).
 enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide };
 
+// Which kernels run the experts, by the average rows per expert (measured on
+// MI355X at d = 4096, d_ff = 14336, E = 8, k = 2; layer times in us):
+//   T        96    128   192   256   512   1024
+//   stream   459   815  1145  1300  2056  3676
+//   grouped  605   615   632   867  1254  1892
+//   wide     653   659   669   690   722   954
+// The weight stream wins while one 32-row token tile holds every expert's
+// rows (at 32 per expert on average half the experts need two, which
+// streams their weights twice); the large tiles win from about 56 rows per
+// expert on, since smaller tiles re-read the weights for every token tile.
 static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
     const int64_t per_expert = A / E;
-    if (per_expert <= 32)
-        return (dt == 1 && stream_supported(A, d, d_ff, E)) ? FfnPath::kStream : FfnPath::kSkinny;
+    const bool stream = dt == 1 && stream_supported(A, d, d_ff, E);
+    if (stream && per_expert <= 24) return FfnPath::kStream;
+    if (dt == 1 && per_expert > 48 && wide_supported(A, d, d_ff)) return FfnPath::kWide;
+    if (per_expert <= 32 && !stream) return FfnPath::kSkinny;
     if (per_expert <= 256) return FfnPath::kGroupedSmall;
-    if (dt == 1 && wide_supported(A, d, d_ff)) return FfnPath::kWide;
     return FfnPath::kGroupedLarge;
 }
 

@@ -66,6 +66,8 @@ SMALL = [
     # workgroups (the ring crosses tile boundaries), 2 K ranges of 512 in
     # GEMM1 and 10 in GEMM2
     Workload("stream-tiles", 23, T=24, d=1024, d_ff=5120),
+    # 25-48 rows per expert: the grouped kernels with 128 x 64 tiles (bf16)
+    Workload("grouped-bf16", 26, T=160, d=512, d_ff=1024),
 ]
 
 
@@ -185,9 +187,9 @@ def test_pieces_expert_ffn_and_combine():
 
 @pytest.mark.parametrize("w", [
     Workload("forced", 20, T=200, d=256, d_ff=512),
-    # decode-sized (T*k/E <= 32): the weight-streaming kernels, here with four
-    # token tiles of 32 rows for each of the two experts
-    Workload("forced-stream", 21, T=128, d=512, d_ff=1024),
+    # decode-sized (T*k/E <= 24): the weight-streaming kernels, here with
+    # three token tiles of 32 rows for each of the two experts
+    Workload("forced-stream", 21, T=96, d=512, d_ff=1024),
 ], ids=lambda w: w.name)
 def test_all_tokens_to_two_experts_and_untouched_experts(w):
     """Every token routes to experts 3 and 5; the other six get no rows, and
