@@ -17,7 +17,8 @@
 // TPW*EG*6.  The fp32 scores land in LDS; lane t < TPW
 // then picks the top k of token t (strict '>' over ascending expert index, so
 // equal fp32 scores go to the lower index) and the gates
-// g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+// g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).  From 1024 tokens on,
+// router_topk_lds_kernel does the same per token with Wg held in LDS.
 #include "gemm_common.h"
 
 namespace moe {
