@@ -68,6 +68,10 @@ SMALL = [
     Workload("stream-tiles", 23, T=24, d=1024, d_ff=5120),
     # 25-48 rows per expert: the grouped kernels with 128 x 64 tiles (bf16)
     Workload("grouped-bf16", 26, T=160, d=512, d_ff=1024),
+    # degenerate routing: one expert (every gate is 1), and every token
+    # taking all eight experts
+    Workload("e1-k1", 27, T=50, d=256, d_ff=512, E=1, k=1),
+    Workload("k-all", 28, T=40, d=256, d_ff=256, E=8, k=8),
 ]
 
 
