@@ -10,7 +10,10 @@
 // each owning 128 x 128 outputs in 256 accumulator registers (one wave per
 // SIMD) as 8 x 8 fragments of v_mfma_f32_16x16x32_bf16, the MFMA form that
 // sustains the most throughput on random data.  Per 32-wide k-step a wave
-// reads eight weight and eight token fragments and issues 64 MFMAs.
+// reads eight weight and eight token fragments and issues 64 MFMAs.  When
+// the experts hold about 100 rows or fewer, a second instantiation uses
+// 128-row token tiles (128 x 64 per wave, 8 x 4 fragments), so less of
+// each tile is padding.
 //
 // k-loop.  A stage is 64 k: one whole 128-byte line of every weight and token
 // row, fetched by global_load_lds (eight lines per instruction) into a
@@ -44,18 +47,26 @@ namespace moe {
 
 namespace {
 
-constexpr int kWideBW = 256, kWideBT = 256, kWideWaves = 4;
+constexpr int kWideBW = 256, kWideWaves = 4;
 constexpr int kWideP = 2;  // stages in the ring (double buffer)
-constexpr int kWideRows = kWideBW + kWideBT;
-constexpr int kWideLPW = kWideRows / 8 / kWideWaves;  // 8-row loads per wave per stage
-constexpr int kWideStageBytes = kWideRows * 128;
 constexpr int kWidePfBytes = 256;  // where the L2 prefetches land (never read)
-constexpr int kWideLds = kWideP * kWideStageBytes + kWidePfBytes;
+// The token-tile height BT: 256, or 128 when the experts hold about 100 rows
+// or fewer (most of a 256-row tile would be padding).
+template <int BT>
+struct WideTile {
+    static constexpr int kRows = kWideBW + BT;
+    static constexpr int kLPW = kRows / 8 / kWideWaves;  // 8-row loads per wave per stage
+    static constexpr int kStageBytes = kRows * 128;
+    static constexpr int kLds = kWideP * kStageBytes + kWidePfBytes;
+    static constexpr int kNJ = BT / 32;  // token fragments per wave
+    static constexpr int kFW = 8 * kNJ;  // fragments per wave
+    static_assert(kLPW * (kWideP - 1) < 64, "vmcnt range");
+    static_assert(kLds <= 160 * 1024 - 1024, "LDS capacity");
+};
 constexpr int kWidePfAhead = 2;   // stages past the one being loaded
 constexpr int kWideKStep = 64;                   // bf16 K elements per stage
-constexpr int kSlotFloats = kWideWaves * kWave * 256;  // accumulators of one workgroup
-static_assert(kWideLPW * (kWideP - 1) < 64, "vmcnt range");
-static_assert(kWideLds <= 160 * 1024 - 1024, "LDS capacity");
+// A scratch slot: the accumulators of one workgroup of 256-row tiles.
+constexpr int kSlotFloats = kWideWaves * kWave * 4 * WideTile<256>::kFW;
 
 // Byte offset of 16-byte chunk c of row r in a stage of 128-byte rows: the
 // chunk sits at c ^ ((r >> 1) & 7), so a 32-row operand read (16 lanes per
@@ -65,12 +76,13 @@ __device__ __forceinline__ int swz128(int r, int c) {
 }
 
 // Per-expert tile table in LDS: first row, row count, first tile number.
+template <int BT>
 struct TileTable {
     int *lo, *cnt, *first;
     int E;
     // Called by one whole wave; the caller syncs.
     __device__ void build(const int32_t *offsets, int A, int col_tiles) {
-        build_expert_table(offsets, E, A, kWideBT, col_tiles, lo, cnt, first);
+        build_expert_table(offsets, E, A, BT, col_tiles, lo, cnt, first);
     }
     // The table is the same for every lane: reading it through
     // readfirstlane keeps the tile and segment arithmetic in scalar
@@ -82,12 +94,12 @@ struct TileTable {
         while (i + 1 < E && u(first[i + 1]) <= t) ++i;
         const int rem = t - u(first[i]);
         const int c = u(cnt[i]), l = u(lo[i]);
-        const int mtiles = (c + kWideBT - 1) / kWideBT;
+        const int mtiles = (c + BT - 1) / BT;
         TileInfo ti;
         ti.e = i;
         ti.mt = rem % mtiles;
-        ti.row0 = l + ti.mt * kWideBT;
-        ti.mrem = min(kWideBT, l + c - ti.row0);
+        ti.row0 = l + ti.mt * BT;
+        ti.mrem = min(BT, l + c - ti.row0);
         ti.n0 = (rem / mtiles) * cols;
         return ti;
     }
@@ -145,14 +157,15 @@ __device__ __forceinline__ void store_fragment(TO *__restrict__ out, int N, cons
 }
 
 // Says that every accumulator is in an accumulator register here.
-__device__ __forceinline__ void pin_accumulators(f32x4 (&acc)[8][8]) {
+template <int NJ>
+__device__ __forceinline__ void pin_accumulators(f32x4 (&acc)[8][NJ]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
-// Scratch slot layout: fragment p = 8 i + j (0..63) of thread t at float4
+// Scratch slot layout: fragment p = NJ i + j of thread t at float4
 // p * 256 + t, so every store and load of a wave is 1 KiB contiguous.
 __device__ __forceinline__ float *slot_ptr(float *partial, int slot) {
     return partial + (size_t)slot * kSlotFloats;
@@ -160,13 +173,15 @@ __device__ __forceinline__ float *slot_ptr(float *partial, int slot) {
 
 }  // namespace
 
-template <bool SWIGLU, typename TO>
+template <bool SWIGLU, typename TO, int BT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void wide_gemm_kernel(
     const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ gather,
     const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb,
     const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out,
     float *__restrict__ partial) {
-    constexpr int P = kWideP, LPW = kWideLPW, BW = kWideBW;
+    using C = WideTile<BT>;
+    constexpr int P = kWideP, LPW = C::kLPW, BW = kWideBW, NJ = C::kNJ, FW = C::kFW;
+    constexpr int kWideStageBytes = C::kStageBytes;
     constexpr int kCols = SWIGLU ? BW / 2 : BW;  // output columns per tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     __shared__ int s_lo[64], s_cnt[64], s_first[65];
@@ -178,7 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int n_k = K / kWideKStep;  // >= P, checked by the launcher
 
-    TileTable tt{s_lo, s_cnt, s_first, E};
+    TileTable<BT> tt{s_lo, s_cnt, s_first, E};
     if (wave == 0) tt.build(offsets, A, (N + kCols - 1) / kCols);
     __syncthreads();
 
@@ -228,7 +243,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = 0; i < LPW; ++i) {
             const int r = (wave + kWideWaves * i) * 8 + (lane >> 3);
             const int c = (lane & 7) ^ ((r >> 1) & 7);
-            if (i < LPW / 2) {
+            if (i < BW / 32) {
                 const int rr = SWIGLU ? r % (BW / 2) : r;  // row within the tile's rows of W
                 off[i] = (uint32_t)(min(ti.n0 + rr, N - 1) - ti.n0) * (uint32_t)(K * 2) + c * 16;
             } else {
@@ -257,11 +272,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int lr = lane & 15, lq = lane >> 4, lx = (lr >> 1) & 7;
     const int roff[2] = {lr * 128 + ((lq ^ lx) << 4), lr * 128 + (((4 + lq) ^ lx) << 4)};
 
-    f32x4 acc[8][8];
-    i32x4 a0[8], b0[8], a1[8], b1[8];
+    f32x4 acc[8][NJ];
+    i32x4 a0[8], b0[NJ], a1[8], b1[NJ];
     // Fragment read k of k-step s (k < 8: weight fragment k, else token
     // fragment k - 8) from a slot.
-    auto read_frag = [&](i32x4 (&a)[8], i32x4 (&b)[8], int slot, int s, int k)
+    auto read_frag = [&](i32x4 (&a)[8], i32x4 (&b)[NJ], int slot, int s, int k)
         __attribute__((always_inline)) {
         const char *base = smem + slot * kWideStageBytes + roff[s];
         if (k < 8)
@@ -269,12 +284,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         else
             b[k - 8] = *(const i32x4 *)(base + trow(k - 8) * 128);
     };
-    // MFMAs [m0, m1) of a k-step, fragment (m / 8, m % 8) for MFMA m.
-    auto mma_part = [&](const i32x4 (&a)[8], const i32x4 (&b)[8], int m0, int m1)
+    // MFMAs [m0, m1) of a k-step, fragment (m / NJ, m % NJ) for MFMA m.
+    auto mma_part = [&](const i32x4 (&a)[8], const i32x4 (&b)[NJ], int m0, int m1)
         __attribute__((always_inline)) {
 #pragma unroll
         for (int m = m0; m < m1; ++m)
-            acc[m / 8][m % 8] = mma16(a[m / 8], b[m % 8], acc[m / 8][m % 8]);
+            acc[m / NJ][m % NJ] = mma16(a[m / NJ], b[m % NJ], acc[m / NJ][m % NJ]);
     };
 
     // The producer runs P stages ahead of the consumer with its own cursor:
@@ -312,7 +327,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     // The loads of one stage into LDS slot dst, then the bases move on.
     auto load_stage = [&](char *dst, int i) __attribute__((always_inline)) {
-        dma16(pb[i < LPW / 4 ? 0 : i < LPW / 2 ? 1 : 2] + po[i], dst + (wave + kWideWaves * i) * 1024);
+        dma16(pb[i < BW / 64 ? 0 : i < BW / 32 ? 1 : 2] + po[i], dst + (wave + kWideWaves * i) * 1024);
     };
     auto advance = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
+            for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{};
         pin_accumulators(acc);
         // The k-loop of one segment.  Each step is cut into chunks by
         // scheduling barriers, so every read and load issues between the
@@ -362,16 +377,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // Step 0 of the segment's first stage (the previous segment read it
         // too, but the ring may have moved on since).
 #pragma unroll
-        for (int k = 0; k < 16; ++k) read_frag(a0, b0, g % P, 0, k);
+        for (int k = 0; k < 8 + NJ; ++k) read_frag(a0, b0, g % P, 0, k);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         for (int s = cur.sb; s < cur.se; ++s, ++g) {
             const int slot = g % P;
             // Step 0 under the reads of step 1, one per MFMA, so the last
-            // read has 48 MFMAs to land under.
+            // read has FW - 8 - NJ MFMAs to land under.
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int m = 0; m < 64; ++m) {
-                if (m < 16) read_frag(a1, b1, slot, 1, m);
+            for (int m = 0; m < FW; ++m) {
+                if (m < 8 + NJ) read_frag(a1, b1, slot, 1, m);
                 mma_part(a0, b0, m, m + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -382,16 +397,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             wait_vmcnt_lgkm0<(LPW + 1) * (P - 2) + 1>();
             stage_barrier();
             // Step 1 under the reads of the next stage's step 0 (one per two
-            // MFMAs, so the last has 32 to land under) and the loads refilling
-            // this slot P stages ahead (one per four MFMAs, spread over the
-            // whole step so the load path never backs up into the issue).
-            static_assert(LPW == 16, "one load per four MFMAs");
+            // MFMAs) and the loads refilling this slot P stages ahead (spread
+            // evenly over the whole step, one per four MFMAs for 256-row
+            // tiles, so the load path never backs up into the issue).
             char *dst = smem + slot * kWideStageBytes;
 #pragma unroll
-            for (int m = 0; m < 64; ++m) {
-                if (m % 2 == 0 && m < 32) read_frag(a0, b0, (g + 1) % P, 0, m / 2);
-                if (m % 4 == 0) load_stage(dst, m / 4);
-                if (m == 63) {
+            for (int m = 0; m < FW; ++m) {
+                if (m % 2 == 0 && m / 2 < 8 + NJ) read_frag(a0, b0, (g + 1) % P, 0, m / 2);
+#pragma unroll
+                for (int l = 0; l < LPW; ++l)
+                    if ((l * FW) / LPW == m) load_stage(dst, l);
+                if (m == FW - 1) {
                     advance();
                     prefetch();
                 }
@@ -413,7 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     asm volatile("" : "+a"(acc[i][j]));
                     if constexpr (SWIGLU) asm volatile("" : "+a"(acc[i + 4][j]));
                     store_fragment<SWIGLU, TO>(out, N, ti, wn, wm, lane, i, j, acc[i][j],
@@ -426,9 +442,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     asm volatile("" : "+a"(acc[i][j]));
-                    const int p = 8 * i + j;
+                    const int p = NJ * i + j;
                     *(f32x4 *)(dst + 4 * (p * 256 + tid)) = acc[i][j];
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -439,11 +455,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // Sums the parts of every split tile in workgroup order and applies the
-// epilogue.  Block b handles fragments 4 (b % 16) .. + 4 of every wave
-// (GEMM1: u fragments, with their v fragments 32 further; the other eight
-// blocks exit) of tile b / 128 of the split round of XCD (b / 16) % 8: a
-// few fragments per block keep many loads in flight.
-template <bool SWIGLU, typename TO>
+// epilogue.  With FB = FW / 4 blocks per tile (16 for 256-row tiles), block b
+// handles fragments 4 (b % FB) .. + 4 of every wave (GEMM1: u fragments,
+// with their v fragments FW / 2 further; the other half of the blocks exit)
+// of tile b / (8 FB) of the split round of XCD (b / FB) % 8: a few fragments
+// per block keep many loads in flight.
+template <bool SWIGLU, typename TO, int BT>
 __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restrict__ offsets,
                                                          int E, int N, int K, int A, int G8,
                                                          TO *__restrict__ out,
@@ -453,9 +470,10 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
     __shared__ int s_slots[64], s_nparts;  // G8 <= 64: one part per workgroup at most
     const int tid = threadIdx.x;
     const int n_k = K / kWideKStep;
-    TileTable tt{s_lo, s_cnt, s_first, E};
-    const int frag = blockIdx.x % 16, xcd = (blockIdx.x / 16) % 8, jr = blockIdx.x / 128;
-    if (SWIGLU && frag >= 8) return;
+    constexpr int NJ = WideTile<BT>::kNJ, FW = WideTile<BT>::kFW, FB = FW / 4;
+    TileTable<BT> tt{s_lo, s_cnt, s_first, E};
+    const int frag = blockIdx.x % FB, xcd = (blockIdx.x / FB) % 8, jr = blockIdx.x / (8 * FB);
+    if (SWIGLU && frag >= FB / 2) return;
     if (tid < kWave) tt.build(offsets, A, (N + kCols - 1) / kCols);
     __syncthreads();
     const XcdShare xs(tt.total(), xcd, G8, n_k, n_k % kWideP == 0);
@@ -495,10 +513,10 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
     };
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int p = 4 * frag + q;  // GEMM1: u fragment (p < 32); GEMM2: any fragment
+        const int p = 4 * frag + q;  // GEMM1: u fragment (p < FW / 2); GEMM2: any fragment
         const f32x4 u = load_sum(p);
-        const f32x4 v = SWIGLU ? load_sum(p + 32) : u;
-        store_fragment<SWIGLU, TO>(out, N, ti, wn, wm, lane, p / 8, p % 8, u, v);
+        const f32x4 v = SWIGLU ? load_sum(p + FW / 2) : u;
+        store_fragment<SWIGLU, TO>(out, N, ti, wn, wm, lane, p / NJ, p % NJ, u, v);
     }
 }
 
@@ -507,21 +525,37 @@ namespace {
 // one workgroup per CU, a multiple of 8 (one share per XCD), at most 64 per XCD
 int wide_grid() { return std::max(8, std::min(device_cus(), 512) / 8 * 8); }
 
+template <bool SWIGLU, typename TO, int BT>
+hipError_t launch_wide_bt(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
+                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
+                          void *out, float *partial, hipStream_t s) {
+    using C = WideTile<BT>;
+    auto kern = wide_gemm_kernel<SWIGLU, TO, BT>;
+    hipError_t err = set_lds_limit<wide_gemm_kernel<SWIGLU, TO, BT>>(C::kLds);
+    if (err != hipSuccess) return err;
+    const int grid = wide_grid();
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), C::kLds, s, (const bf16_t *)act, act_ld,
+                       gather, (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
+                       (TO *)out, partial);
+    if ((err = hipGetLastError()) != hipSuccess || !partial) return err;
+    hipLaunchKernelGGL((wide_fixup_kernel<SWIGLU, TO, BT>), dim3(grid * (C::kFW / 4)), dim3(256),
+                       0, s, offsets, E, N, K, (int)A, grid / 8, (TO *)out,
+                       (const float *)partial);
+    return hipGetLastError();
+}
+
+// 128-row token tiles up to 100 rows per expert on average (measured on
+// MI355X with d = 4096, d_ff = 14336, E = 8: 16 % faster at 57-96 rows, 10 %
+// slower from 128 on, where 256-row tiles are fuller), else 256.
 template <bool SWIGLU, typename TO>
 hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                        const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
                        void *out, float *partial, hipStream_t s) {
-    auto kern = wide_gemm_kernel<SWIGLU, TO>;
-    hipError_t err = set_lds_limit<wide_gemm_kernel<SWIGLU, TO>>(kWideLds);
-    if (err != hipSuccess) return err;
-    const int grid = wide_grid();
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), kWideLds, s, (const bf16_t *)act, act_ld,
-                       gather, (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
-                       (TO *)out, partial);
-    if ((err = hipGetLastError()) != hipSuccess || !partial) return err;
-    hipLaunchKernelGGL((wide_fixup_kernel<SWIGLU, TO>), dim3(grid * 16), dim3(256), 0, s, offsets,
-                       E, N, K, (int)A, grid / 8, (TO *)out, (const float *)partial);
-    return hipGetLastError();
+    if (A <= 100 * (int64_t)E)
+        return launch_wide_bt<SWIGLU, TO, 128>(act, act_ld, gather, Wa, Wb, offsets, E, N, K, A,
+                                               out, partial, s);
+    return launch_wide_bt<SWIGLU, TO, 256>(act, act_ld, gather, Wa, Wb, offsets, E, N, K, A, out,
+                                           partial, s);
 }
 
 }  // namespace
