@@ -484,3 +484,35 @@ def test_route_balance_rejects_empty_batch():
     Wg = torch.zeros((8, 128), dtype=torch.float32, device=DEV)
     with pytest.raises(moe.MoeError):
         moe.moe_route_balance(x, Wg, 2, ws=torch.empty(256, dtype=torch.uint8, device=DEV))
+
+
+# ------------------------------------------------------ random shapes
+
+def _random_workload(seed):
+    """A seeded random layer shape within the library's limits: any expert
+    count and k, d and d_ff multiples of 64, a quarter fp32; odd seeds take
+    shapes the weight-streaming kernels accept (d, d_ff multiples of 512,
+    small batches)."""
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.choice([1, 2, 3, 4, 8, 8, 13, 16, 64]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    if seed % 2:
+        d = int(rng.choice([512, 1024, 1536]))
+        d_ff = int(rng.choice([512, 1024, 1536, 2048]))
+        T = int(rng.choice([1, 3, 8, 24, 48, 96]))
+    else:
+        d = int(rng.integers(1, 17)) * 64
+        d_ff = int(rng.integers(1, 33)) * 64
+        T = int(rng.choice([2, 17, 64, 150, 400, 1100]))
+    dt = "f32" if rng.random() < 0.25 else "bf16"
+    return Workload(f"random-{seed}", 200 + seed, T=T, d=d, d_ff=d_ff, E=E, k=k, dtype=dt)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    """moe_forward on seeded random shapes (every kernel family and their
+    thresholds) against the oracle on up to 48 sampled tokens."""
+    w = _random_workload(seed)
+    L = _case(w)
+    rows = None if w.T <= 48 else np.sort(np.random.default_rng(seed).choice(w.T, 48, replace=False))
+    _forward_and_check(w, L, rows=rows)
