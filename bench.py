@@ -283,7 +283,12 @@ def main():
     roofline = None
     if blocks is None:
         gemm1_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
-        if (w.T * w.k) // w.E <= 32:   # weight streaming (the skinny kernels): HBM-bound
+        # bound by the GEMM's arithmetic intensity on its weights (2 flop per
+        # weight element per row of the expert) against the chip's ridge
+        es = 4 if w.dtype == "f32" else 2
+        peak_fl = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        per_expert = (w.T * w.k) // w.E
+        if 2 * per_expert / es < peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9):   # HBM-bound
             achieved = g_bytes / (gemm1_ms * 1e-3) / 1e9
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -294,15 +299,16 @@ def main():
             roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
         roofline["traffic"] = measured_traffic(w.name)
-        per_expert = (w.T * w.k) // w.E
-        if per_expert <= 32:
-            kname = ("stream_gemm_kernel<SWIGLU>"
-                     if w.dtype == "bf16" and min(w.d, w.d_ff) >= 352 else
-                     "skinny_gemm_kernel<SWIGLU>")
-        elif per_expert <= 256 or w.dtype == "f32":
-            kname = "grouped_gemm_kernel<SWIGLU>"
-        else:
+        # the library's choice of expert kernels (by rows per expert)
+        stream_ok = w.dtype == "bf16" and w.d % 512 == 0 and w.d_ff % 512 == 0
+        if stream_ok and per_expert <= 24:
+            kname = "stream_gemm_kernel<SWIGLU>"
+        elif w.dtype == "bf16" and per_expert > 48:
             kname = "wide_gemm_kernel<SWIGLU>"
+        elif per_expert <= 32 and not stream_ok:
+            kname = "skinny_gemm_kernel<SWIGLU>"
+        else:
+            kname = "grouped_gemm_kernel<SWIGLU>"
         roofline["kernel"] = kname + " (W1/W3 + silu*v)"
         roofline["kernel_ms"] = round(gemm1_ms, 4)
         roofline["alg_bytes"] = g_bytes
@@ -310,6 +316,24 @@ def main():
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
+
+    # Where a layer's time goes: a few more layers, outside the timed region,
+    # with the library's events around every stage (recording all six costs
+    # the layer about 10 us, so the timed steps carry only GEMM1's pair).
+    breakdown = None
+    if blocks is None:
+        marks = [[ev.create() for _ in range(6)] for _ in range(10)]
+        for _ in range(10):   # back to the steady state after the pause above
+            step(none6)
+        for m in marks:
+            step(m)
+        torch.cuda.synchronize()
+        names = ["router", "dispatch", "gemm1", "gemm2", "combine"]
+        breakdown = {n: round(float(np.mean([ev.elapsed_ms(m[i], m[i + 1]) for m in marks])) * 1e3, 1)
+                     for i, n in enumerate(names)}
+        for m in marks:
+            for e in m:
+                ev.destroy(e)
 
     step_s = ms_per_step * 1e-3
     nblk = max(1, w.blocks)
@@ -339,6 +363,8 @@ def main():
                    "seed": args.seed},
         "roofline": roofline, "cpu_baseline": cpu, "layer_roofline": layer,
     }
+    if breakdown is not None:
+        out["stage_us"] = breakdown
     if sweep is not None:
         out["decode_sweep"] = sweep
     print(json.dumps(out), flush=True)
