@@ -355,9 +355,9 @@ __global__ __launch_bounds__(1024) void balance_reduce_kernel(
 namespace {
 
 // Few tokens: four waves split each token's row, so a small batch still
-// spreads over many waves.  Many tokens: one wave per token, four tokens per
-// workgroup (measured on MI355X: 29 us against 46 us for four tokens per
-// wave at T = 4096; 7.7 us against 16.7 us the other way at T = 32).
+// spreads over many waves (at T = 32 on MI355X: 7.2 us inside the layer,
+// against 8.9 us with sixteen waves per token and 16.7 us with one).  Many
+// tokens: one wave per token, four tokens per workgroup, or the LDS kernel.
 bool router_wide_rows(int64_t T) { return T < 1024; }
 
 template <typename Tin, int Q>
@@ -398,19 +398,7 @@ hipError_t launch_router_impl(const void *x, int dt, const float *Wg, int64_t T,
         if (dt == 0) return launch_router_lds((const float *)x, Wg, T, d, E, k, idx, gw, logits, s);
         return launch_router_lds((const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, s);
     }
-    if (T <= 256 && d % (16 * 8) == 0) {
-        // decode sizes: sixteen waves split each token's row, so the few
-        // tokens still spread over the chip
-        const dim3 block16(16 * kWave);
-        if (dt == 0)
-            hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 16, STATS, 16>), grid, block16, 0,
-                               s, (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p,
-                               part_c);
-        else
-            hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 16, STATS, 16>), grid, block16,
-                               0, s, (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, part_p,
-                               part_c);
-    } else if (router_wide_rows(T)) {
+    if (router_wide_rows(T)) {
         if (dt == 0)
             hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 4, STATS>), grid, block, 0, s,
                                (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p, part_c);
