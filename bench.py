@@ -181,6 +181,124 @@ def decode_sweep(w, L, moe, np, torch, stream, steps):
     return res
 
 
+def routing_summary(w, L, moe, np, torch):
+    """What the batch's routing looks like, from the GPU router's own fp32
+    scores: experts in use, the share of assignments on experts 0 and 1 (the
+    skewed workload aims at about half), and the tokens whose k-th and
+    (k+1)-th scores (set) or kept scores (order) are closer than 1e-6 --
+    the near ties that the exact routing comparison exempts."""
+    T, E, k = w.T, w.E, w.k
+    logits = torch.empty((T, E), dtype=torch.float32, device=L["x"].device)
+    idx, _ = moe.moe_route(L["x"], L["Wg"], k, logits=logits)
+    torch.cuda.synchronize()
+    lg = np.sort(logits.cpu().numpy().astype(np.float64), axis=1)[:, ::-1]
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=E)
+    gap_set = lg[:, k - 1] - lg[:, k] if k < E else np.full(T, np.inf)
+    gap_order = (np.diff(-lg[:, :k], axis=1).min(axis=1) if k > 1 else np.full(T, np.inf))
+    return counts, {"active_experts": int((counts > 0).sum()),
+                    "experts01_share": round(float(counts[:2].sum() / counts.sum()), 4),
+                    "near_ties_set": int((gap_set < 1e-6).sum()),
+                    "near_ties_order": int((gap_order < 1e-6).sum())}
+
+
+def gemm1_roofline(w, counts, gemm1_ms, kernel):
+    """The dominant kernel (the W1/W3 + SwiGLU GEMM) against its roofline:
+    HBM when its arithmetic intensity on the weights (2 flop per weight
+    element per row of the expert) is below the chip's ridge, else MFMA."""
+    g_bytes, g_flops, _ = gemm1_work(w, counts)
+    es = 4 if w.dtype == "f32" else 2
+    peak_fl = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    per_expert = (w.T * w.k) // w.E
+    if 2 * per_expert / es < peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = g_bytes / (gemm1_ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = g_flops / (gemm1_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_fl,
+             "unit": "TFLOP/s", "frac": round(achieved / peak_fl, 4)}
+    r["traffic"] = measured_traffic(w.name)
+    r["kernel"] = kernel + " GEMM1 (W1/W3 + silu*v)"
+    r["kernel_ms"] = round(gemm1_ms, 4)
+    r["alg_bytes"] = g_bytes
+    r["alg_flops"] = g_flops
+    return r
+
+
+def layer_roofline(w, n_active, ms_per_step):
+    l_bytes, l_flops = layer_work(w, n_active)
+    nblk = max(1, w.blocks)
+    step_s = ms_per_step * 1e-3
+    peak_fl = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    return {"alg_bytes": l_bytes * nblk, "alg_flops": l_flops * nblk,
+            "hbm_frac": round(l_bytes * nblk / step_s / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_frac": round(l_flops * nblk / step_s / 1e12 / peak_fl, 4),
+            "active_experts": n_active}
+
+
+def time_layer(w, L, moe, np, torch, ev, stream, steps, warmup, blocks=None):
+    """W untimed layers, then K timed ones between two synchronisations.
+    Returns (ms per step, mean GEMM1 ms from the library's events around
+    that kernel in every timed step, stage breakdown in us or None)."""
+    dev = L["x"].device
+    ws = moe.workspace(w.T, w.d, w.d_ff, w.E, w.k, L["x"].dtype, dev)
+    y = torch.empty_like(L["x"])
+    eps = float(np.float32(w.eps))
+
+    def step(marks):
+        if blocks is None:
+            moe.moe_forward_profiled(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.k, marks,
+                                     y=y, ws=ws, stream=stream)
+        else:
+            h = y
+            h.copy_(L["x"])
+            for B in blocks:
+                moe.moe_block_forward(h, B["Wg"], B["W1"], B["W3"], B["W2"], w.k, eps, ws=ws,
+                                      stream=stream)
+
+    none6 = [None] * 6
+    for _ in range(warmup):
+        step(none6)
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup done", file=sys.stderr, flush=True)
+
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step([None, None, pairs[i][0], pairs[i][1], None, None] if blocks is None else none6)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    print(f"[bench] {w.name}: timed {steps} steps, {ms_per_step:.3f} ms/step", file=sys.stderr,
+          flush=True)
+    gemm1_ms = None
+    if blocks is None:
+        gemm1_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    # Where a layer's time goes: a few more layers, outside the timed region,
+    # with the library's events around every stage (recording all six costs
+    # the layer about 10 us, so the timed steps carry only GEMM1's pair).
+    breakdown = None
+    if blocks is None:
+        marks = [[ev.create() for _ in range(6)] for _ in range(10)]
+        for _ in range(10):   # back to the steady state after the pause above
+            step(none6)
+        for m in marks:
+            step(m)
+        torch.cuda.synchronize()
+        names = ["router", "dispatch", "gemm1", "gemm2", "combine"]
+        breakdown = {n: round(float(np.mean([ev.elapsed_ms(m[i], m[i + 1]) for m in marks])) * 1e3, 1)
+                     for i, n in enumerate(names)}
+        for m in marks:
+            for e in m:
+                ev.destroy(e)
+    return ms_per_step, gemm1_ms, breakdown
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +313,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-sweep", action="store_true",
                     help="skip the T = 1..16 small-batch lines of the decode workload")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill (T = 4096) layer the decode run also times")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="oracle sample size (default sized to ~10-30 s)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -241,111 +361,39 @@ def main():
     torch.cuda.synchronize()
     print("[bench] inputs ready", file=sys.stderr, flush=True)
 
-    ws = moe.workspace(w.T, w.d, w.d_ff, w.E, w.k, L["x"].dtype, dev)
-    y = torch.empty_like(L["x"])
-    eps = float(np.float32(w.eps))
+    ms_per_step, gemm1_ms, breakdown = time_layer(w, L, moe, np, torch, ev, stream, args.steps,
+                                                  args.warmup, blocks)
+    tokens_per_s = w.T / (ms_per_step * 1e-3)
 
-    def step(marks):
-        if blocks is None:
-            moe.moe_forward_profiled(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.k, marks,
-                                     y=y, ws=ws, stream=stream)
-        else:
-            h = y
-            h.copy_(L["x"])
-            for B in blocks:
-                moe.moe_block_forward(h, B["Wg"], B["W1"], B["W3"], B["W2"], w.k, eps, ws=ws,
-                                      stream=stream)
-
-    none6 = [None] * 6
-    for _ in range(args.warmup):
-        step(none6)
-    torch.cuda.synchronize()
-    print("[bench] warmup done", file=sys.stderr, flush=True)
-
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step([None, None, pairs[i][0], pairs[i][1], None, None] if blocks is None else none6)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    tokens_per_s = w.T * args.steps / (t1 - t0)
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr,
-          flush=True)
-
-    # routing of this batch (for the active-expert count of the byte model)
-    idx, _ = moe.moe_route(L["x"], L["Wg"], w.k)
-    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.E)
-    g_bytes, g_flops, n_active = gemm1_work(w, counts)
-    l_bytes, l_flops = layer_work(w, n_active)
-
-    roofline = None
-    if blocks is None:
-        gemm1_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
-        # bound by the GEMM's arithmetic intensity on its weights (2 flop per
-        # weight element per row of the expert) against the chip's ridge
-        es = 4 if w.dtype == "f32" else 2
-        peak_fl = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-        per_expert = (w.T * w.k) // w.E
-        if 2 * per_expert / es < peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9):   # HBM-bound
-            achieved = g_bytes / (gemm1_ms * 1e-3) / 1e9
-            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                        "traffic": None}
-        else:
-            peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-            achieved = g_flops / (gemm1_ms * 1e-3) / 1e12
-            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
-        roofline["traffic"] = measured_traffic(w.name)
-        # the library's choice of expert kernels (by rows per expert)
-        stream_ok = w.dtype == "bf16" and w.d % 512 == 0 and w.d_ff % 512 == 0
-        if stream_ok and per_expert <= 24:
-            kname = "stream_gemm_kernel<SWIGLU>"
-        elif w.dtype == "bf16" and per_expert > 48:
-            kname = "wide_gemm_kernel<SWIGLU>"
-        elif per_expert <= 32 and not stream_ok:
-            kname = "skinny_gemm_kernel<SWIGLU>"
-        else:
-            kname = "grouped_gemm_kernel<SWIGLU>"
-        roofline["kernel"] = kname + " (W1/W3 + silu*v)"
-        roofline["kernel_ms"] = round(gemm1_ms, 4)
-        roofline["alg_bytes"] = g_bytes
-        roofline["alg_flops"] = g_flops
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
-
-    # Where a layer's time goes: a few more layers, outside the timed region,
-    # with the library's events around every stage (recording all six costs
-    # the layer about 10 us, so the timed steps carry only GEMM1's pair).
-    breakdown = None
-    if blocks is None:
-        marks = [[ev.create() for _ in range(6)] for _ in range(10)]
-        for _ in range(10):   # back to the steady state after the pause above
-            step(none6)
-        for m in marks:
-            step(m)
-        torch.cuda.synchronize()
-        names = ["router", "dispatch", "gemm1", "gemm2", "combine"]
-        breakdown = {n: round(float(np.mean([ev.elapsed_ms(m[i], m[i + 1]) for m in marks])) * 1e3, 1)
-                     for i, n in enumerate(names)}
-        for m in marks:
-            for e in m:
-                ev.destroy(e)
-
-    step_s = ms_per_step * 1e-3
-    nblk = max(1, w.blocks)
-    layer = {"alg_bytes": l_bytes * nblk, "alg_flops": l_flops * nblk,
-             "hbm_frac": round(l_bytes * nblk / step_s / 1e9 / PEAK_HBM_GBS, 4),
-             "mfma_frac": round(l_flops * nblk / step_s / 1e12 /
-                                (PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS), 4),
-             "active_experts": n_active}
+    counts, routing = routing_summary(w, L, moe, np, torch)
+    kernel = moe.moe_expert_ffn_kernels(w.T, w.d, w.d_ff, w.E, w.k, w.torch_dtype)
+    roofline = gemm1_roofline(w, counts, gemm1_ms, kernel) if blocks is None else None
+    layer = layer_roofline(w, routing["active_experts"], ms_per_step)
 
     sweep = None
     if w.name == "decode" and not args.no_decode_sweep:
         sweep = decode_sweep(w, L, moe, np, torch, stream, args.steps)
+
+    # The compute-bound half of the metric: the prefill layer (T = 4096) timed
+    # the same way, reported beside the decode headline.
+    prefill = None
+    if w.name == "decode" and not args.no_prefill:
+        wp = WORKLOADS["prefill"]
+        Lp = make_layer(wp, dev, args.seed)
+        torch.cuda.synchronize()
+        p_ms, p_g1, p_stages = time_layer(wp, Lp, moe, np, torch, ev, stream, args.steps,
+                                          args.warmup)
+        p_counts, p_routing = routing_summary(wp, Lp, moe, np, torch)
+        p_kernel = moe.moe_expert_ffn_kernels(wp.T, wp.d, wp.d_ff, wp.E, wp.k, wp.torch_dtype)
+        prefill = {"config": {"workload": wp.name, "T": wp.T, "d": wp.d, "d_ff": wp.d_ff,
+                              "E": wp.E, "k": wp.k, "act_dtype": wp.dtype},
+                   "ms_per_step": round(p_ms, 4),
+                   "tokens_per_s": round(wp.T / (p_ms * 1e-3), 1),
+                   "roofline": gemm1_roofline(wp, p_counts, p_g1, p_kernel),
+                   "layer_roofline": layer_roofline(wp, p_routing["active_experts"], p_ms),
+                   "stage_us": p_stages, "routing": p_routing}
+        del Lp
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline and blocks is None:
@@ -361,12 +409,14 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                    "blocks": w.blocks, "act_dtype": w.dtype, "router_dtype": "f32",
                    "seed": args.seed},
-        "roofline": roofline, "cpu_baseline": cpu, "layer_roofline": layer,
+        "roofline": roofline, "cpu_baseline": cpu, "layer_roofline": layer, "routing": routing,
     }
     if breakdown is not None:
         out["stage_us"] = breakdown
     if sweep is not None:
         out["decode_sweep"] = sweep
+    if prefill is not None:
+        out["prefill"] = prefill
     print(json.dumps(out), flush=True)
 
 

@@ -73,6 +73,14 @@ const char *moe_last_error(void);
  * workspace pointer is required. */
 size_t moe_workspace_size(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt);
 
+/* Name of the kernel family that runs the expert GEMMs of moe_forward,
+ * moe_expert_ffn and moe_block_forward for this shape (the choice depends on
+ * the average rows per expert, T*k/E, on dt and on d, d_ff): one of
+ * "stream_gemm_kernel", "skinny_gemm_kernel", "grouped_gemm_kernel (...)",
+ * "wide_gemm_kernel (...)".  Static storage; "" for shapes the library
+ * rejects.  Host only, enqueues nothing. */
+const char *moe_expert_ffn_kernels(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt);
+
 /* Router: scores, top-k and gates for T tokens.
  *   x [T][d] (dt), Wg fp32 [E][d]
  *   -> topk_idx int32 [T][k]: chosen experts, best first; equal fp32 scores

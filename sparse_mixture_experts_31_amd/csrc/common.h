@@ -89,6 +89,8 @@ hipError_t moe_launch_expert_ffn(const void *act, const int32_t *gather, const i
                                  hipEvent_t mid_event, hipStream_t s);
 bool moe_expert_ffn_gathers(int dt, int64_t A, int d, int d_ff, int E);
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E);
+// Name of the kernel family that runs the experts for this shape.
+const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E);
 // The same experts for decode-sized batches (few rows per expert).
 hipError_t moe_launch_skinny_ffn(const void *x_perm, const int32_t *offsets, const void *W1,
                                  const void *W3, const void *W2, int dt, int out_f32, int64_t A,

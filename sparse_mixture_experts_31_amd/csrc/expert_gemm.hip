@@ -358,6 +358,23 @@ bool moe_expert_ffn_gathers(int dt, int64_t A, int d, int d_ff, int E) {
     return moe::path_gathers(moe::ffn_path(dt, A, d, d_ff, E));
 }
 
+const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E) {
+    switch (moe::ffn_path(dt, A, d, d_ff, E)) {
+        case moe::FfnPath::kStream:
+            return "stream_gemm_kernel";
+        case moe::FfnPath::kSkinny:
+            return "skinny_gemm_kernel";
+        case moe::FfnPath::kGroupedSmall:
+            return "grouped_gemm_kernel (128 x 64 tiles)";
+        case moe::FfnPath::kGroupedLarge:
+            return "grouped_gemm_kernel (256 x 256 tiles)";
+        case moe::FfnPath::kWide:
+            return moe::wide_token_tile(A, E) == 128 ? "wide_gemm_kernel (128-row token tiles)"
+                                                     : "wide_gemm_kernel (256-row token tiles)";
+    }
+    return "";
+}
+
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E) {
     switch (moe::ffn_path(dt, A, d, d_ff, E)) {
         case moe::FfnPath::kWide:

@@ -234,9 +234,14 @@ constexpr int kRouterLdsBytes = 128 * 1024;  // most Wg bytes held in LDS
 // the router an L2 stream of T times Wg.  Here a workgroup copies Wg into
 // LDS once and its eight waves walk tokens (wave w of workgroup b: tokens
 // 8 b + w, then a grid further).  A lane covers the same elements of d in
-// the same order with the same fp64 steps and the same wave reduction as in
-// router_topk_kernel, so the scores are the same bit for bit; the token's
-// row is fetched eight pieces at a time so its loads are in flight together.
+// the same order with the same fp64 steps and the same wave reduction as the
+// one-wave-per-token form of router_topk_kernel (WPT = 1, which the load
+// statistics use from 1024 tokens on), so those two give the same scores bit
+// for bit.  Below 1024 tokens both entry points use the four-wave form
+// (WPT = 4), whose fp64 partial sums meet in a different order: a score may
+// then differ from the one-wave form's in its last fp32 bit, rarely.  The
+// token's row is fetched eight pieces at a time so its loads are in flight
+// together.
 template <typename Tin, int Q>
 __global__ __launch_bounds__(kRouterLdsWaves * kWave) void router_topk_lds_kernel(
     const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,

@@ -349,18 +349,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // The K chunks' partial sums added in chunk order (so the sum is the same
 // on every run), then the epilogue: GEMM2 out[r][n] = sum_c o_c[r][n];
 // GEMM1 out[r][n] = silu(sum_c u_c[r][n]) * sum_c v_c[r][n].  Nothing to do
-// when the GEMM kernel chose one chunk.
+// when the GEMM kernel chose one chunk.  Only the rows the experts own,
+// [offsets[0], offsets[E]) clamped to [0, A) as the tile table clamps them,
+// are written: rows outside belong to no tile, their slices hold nothing.
 template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restrict__ part,
-                                                            int64_t A, int N,
+                                                            const int32_t *__restrict__ offsets,
+                                                            int E, int64_t A, int N,
                                                             TO *__restrict__ out) {
     const int kc = *(const int *)part;
     if (kc <= 1) return;
     const float *slices = part + kSPartHdr;
     constexpr int W = SWIGLU ? 2 : 1;
-    const int64_t n4 = A * N / 4;               // N is a multiple of 512
+    const int64_t lo = min<int64_t>(max(offsets[0], 0), A);
+    const int64_t hi = min<int64_t>(max<int64_t>(offsets[E], lo), A);
+    const int64_t n4 = hi * N / 4;              // N is a multiple of 512
     const int64_t slice = A * (int64_t)(W * N);  // floats per chunk
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+    for (int64_t i = lo * N / 4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
          i += (int64_t)gridDim.x * 256) {
         const int64_t r = (4 * i) / N, n = (4 * i) % N;
         const float *p = slices + r * (W * N) + n;
@@ -402,7 +407,7 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather,
     const int64_t n4 = A * N / 4;  // N is a multiple of 512
     const int rgrid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
     hipLaunchKernelGGL((stream_reduce_kernel<SWIGLU, TO>), dim3(rgrid), dim3(256), 0, s,
-                       (const float *)part, A, N, (TO *)out);
+                       (const float *)part, offsets, E, A, N, (TO *)out);
     return hipGetLastError();
 }
 

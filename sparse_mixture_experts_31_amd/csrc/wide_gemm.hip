@@ -551,7 +551,7 @@ template <bool SWIGLU, typename TO>
 hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                        const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
                        void *out, float *partial, hipStream_t s) {
-    if (A <= 100 * (int64_t)E)
+    if (wide_token_tile(A, E) == 128)
         return launch_wide_bt<SWIGLU, TO, 128>(act, act_ld, gather, Wa, Wb, offsets, E, N, K, A,
                                                out, partial, s);
     return launch_wide_bt<SWIGLU, TO, 256>(act, act_ld, gather, Wa, Wb, offsets, E, N, K, A, out,
@@ -559,6 +559,8 @@ hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, c
 }
 
 }  // namespace
+
+int wide_token_tile(int64_t A, int E) { return A <= 100 * (int64_t)E ? 128 : 256; }
 
 size_t wide_partial_bytes() { return (size_t)2 * wide_grid() * kSlotFloats * sizeof(float); }
 

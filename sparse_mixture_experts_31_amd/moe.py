@@ -45,6 +45,8 @@ def lib():
         L.moe_last_error.argtypes = []
         L.moe_workspace_size.restype = sz
         L.moe_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+        L.moe_expert_ffn_kernels.restype = ctypes.c_char_p
+        L.moe_expert_ffn_kernels.argtypes = [i64, i32, i32, i32, i32, i32]
         L.moe_route_balance_workspace_size.restype = sz
         L.moe_route_balance_workspace_size.argtypes = [i64, i32]
         sigs = {
@@ -85,6 +87,37 @@ def _dt(t: torch.Tensor) -> int:
     raise TypeError(f"activations and expert weights must be fp32 or bf16, got {t.dtype}")
 
 
+def _check_router(x, Wg):
+    """Raise before the call if Wg is not the fp32 [E][d] gate matrix of x [T][d]
+    (the library reads E*d fp32 values from it)."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T][d], got shape {tuple(x.shape)}")
+    if Wg.dtype != torch.float32:
+        raise TypeError(f"Wg must be fp32, got {Wg.dtype}")
+    if Wg.dim() != 2 or Wg.shape[1] != x.shape[1]:
+        raise ValueError(f"Wg must be [E][d] with d = {x.shape[1]}, got {tuple(Wg.shape)}")
+
+
+def _check_experts(act, W1, W3, W2):
+    """Raise before the call unless W1, W3 are [E][d_ff][d] and W2 is
+    [E][d][d_ff] in the activations' dtype (d = act's row length)."""
+    d = act.shape[-1]
+    for name, W in (("W1", W1), ("W3", W3), ("W2", W2)):
+        if W.dtype != act.dtype:
+            raise TypeError(f"{name} must have the activations' dtype {act.dtype}, got {W.dtype}")
+        if W.dim() != 3:
+            raise ValueError(f"{name} must be 3-dimensional, got shape {tuple(W.shape)}")
+    E, d_ff, d1 = W1.shape
+    if d1 != d or tuple(W3.shape) != (E, d_ff, d) or tuple(W2.shape) != (E, d, d_ff):
+        raise ValueError(f"expert shapes W1 {tuple(W1.shape)}, W3 {tuple(W3.shape)}, W2 "
+                         f"{tuple(W2.shape)} do not fit d = {d}")
+
+
+def _check_out(name, t, shape, dtype):
+    if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype):
+        raise ValueError(f"{name} must be {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
 def _p(t):
     if t is None:
         return None
@@ -105,6 +138,12 @@ def moe_workspace_size(T, d, d_ff, E, k, dtype) -> int:
     return int(lib().moe_workspace_size(T, d, d_ff, E, k, dt))
 
 
+def moe_expert_ffn_kernels(T, d, d_ff, E, k, dtype) -> str:
+    """Kernel family the library picks for the expert GEMMs of this shape."""
+    dt = MOE_F32 if dtype in (torch.float32, MOE_F32) else MOE_BF16
+    return lib().moe_expert_ffn_kernels(T, d, d_ff, E, k, dt).decode()
+
+
 def workspace(T, d, d_ff, E, k, dtype, device="cuda") -> torch.Tensor:
     n = moe_workspace_size(T, d, d_ff, E, k, dtype)
     if n == 0:
@@ -113,8 +152,12 @@ def workspace(T, d, d_ff, E, k, dtype, device="cuda") -> torch.Tensor:
 
 
 def moe_route(x, Wg, k, topk_idx=None, topk_w=None, logits=None, stream=None):
+    _check_router(x, Wg)
     T, d = x.shape
     E = Wg.shape[0]
+    _check_out("topk_idx", topk_idx, (T, k), torch.int32)
+    _check_out("topk_w", topk_w, (T, k), torch.float32)
+    _check_out("logits", logits, (T, E), torch.float32)
     if topk_idx is None:
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     if topk_w is None:
@@ -131,8 +174,11 @@ def moe_route_balance_workspace_size(T, E) -> int:
 def moe_route_balance(x, Wg, k, topk_idx=None, topk_w=None, ws=None, stream=None):
     """moe_route plus the load statistics: returns (topk_idx, topk_w, f, P,
     laux) with f, P fp32 [E] and laux an fp32 tensor of one element."""
+    _check_router(x, Wg)
     T, d = x.shape
     E = Wg.shape[0]
+    _check_out("topk_idx", topk_idx, (T, k), torch.int32)
+    _check_out("topk_w", topk_w, (T, k), torch.float32)
     if topk_idx is None:
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     if topk_w is None:
@@ -155,6 +201,12 @@ def moe_permute(x, topk_idx, E, counts=None, offsets=None, row_of=None, token_of
     T, d = x.shape
     k = topk_idx.shape[1]
     dev = x.device
+    _check_out("topk_idx", topk_idx, (T, k), torch.int32)
+    _check_out("counts", counts, (E,), torch.int32)
+    _check_out("offsets", offsets, (E + 1,), torch.int32)
+    _check_out("row_of", row_of, (T, k), torch.int32)
+    _check_out("token_of", token_of, (T * k,), torch.int32)
+    _check_out("x_perm", x_perm, (T * k, d), x.dtype)
     counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
     row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
@@ -166,7 +218,11 @@ def moe_permute(x, topk_idx, E, counts=None, offsets=None, row_of=None, token_of
 
 
 def moe_expert_ffn(x_perm, offsets, W1, W3, W2, T, k, out_perm=None, ws=None, stream=None):
+    _check_experts(x_perm, W1, W3, W2)
     E, d_ff, d = W1.shape
+    _check_out("x_perm", x_perm, (T * k, d), x_perm.dtype)
+    _check_out("offsets", offsets, (E + 1,), torch.int32)
+    _check_out("out_perm", out_perm, (T * k, d), x_perm.dtype)
     if out_perm is None:
         out_perm = torch.empty((T * k, d), dtype=x_perm.dtype, device=x_perm.device)
     if ws is None:
@@ -179,6 +235,10 @@ def moe_expert_ffn(x_perm, offsets, W1, W3, W2, T, k, out_perm=None, ws=None, st
 def moe_combine(out_perm, row_of, topk_w, residual=None, y=None, stream=None):
     T, k = row_of.shape
     d = out_perm.shape[1]
+    _check_out("row_of", row_of, (T, k), torch.int32)
+    _check_out("topk_w", topk_w, (T, k), torch.float32)
+    _check_out("residual", residual, (T, d), out_perm.dtype)
+    _check_out("y", y, (T, d), out_perm.dtype)
     if y is None:
         y = torch.empty((T, d), dtype=out_perm.dtype, device=out_perm.device)
     _call("moe_combine", _p(out_perm), _p(row_of), _p(topk_w), _p(residual), _dt(out_perm), T,
@@ -187,8 +247,13 @@ def moe_combine(out_perm, row_of, topk_w, residual=None, y=None, stream=None):
 
 
 def moe_forward(x, Wg, W1, W3, W2, k, y=None, ws=None, stream=None):
+    _check_router(x, Wg)
+    _check_experts(x, W1, W3, W2)
     T, d = x.shape
     E, d_ff, _ = W1.shape
+    if Wg.shape[0] != E:
+        raise ValueError(f"Wg has {Wg.shape[0]} experts, W1 {E}")
+    _check_out("y", y, (T, d), x.dtype)
     if y is None:
         y = torch.empty_like(x)
     if ws is None:
@@ -201,8 +266,13 @@ def moe_forward(x, Wg, W1, W3, W2, k, y=None, ws=None, stream=None):
 def moe_forward_profiled(x, Wg, W1, W3, W2, k, events, y=None, ws=None, stream=None):
     """moe_forward that records 6 caller-owned hipEvent_t handles (ints or
     None) around its stages: router, dispatch, GEMM1, GEMM2, combine."""
+    _check_router(x, Wg)
+    _check_experts(x, W1, W3, W2)
     T, d = x.shape
     E, d_ff, _ = W1.shape
+    if Wg.shape[0] != E:
+        raise ValueError(f"Wg has {Wg.shape[0]} experts, W1 {E}")
+    _check_out("y", y, (T, d), x.dtype)
     if y is None:
         y = torch.empty_like(x)
     if ws is None:
@@ -215,6 +285,7 @@ def moe_forward_profiled(x, Wg, W1, W3, W2, k, events, y=None, ws=None, stream=N
 
 def moe_rmsnorm(h, eps, out=None, stream=None):
     T, d = h.shape
+    _check_out("out", out, (T, d), h.dtype)
     if out is None:
         out = torch.empty_like(h)
     _call("moe_rmsnorm", _p(h), _dt(h), T, d, float(eps), _p(out), _s(stream))
@@ -224,8 +295,14 @@ def moe_rmsnorm(h, eps, out=None, stream=None):
 def moe_block_forward(h, Wg, W1, W3, W2, k, eps, topk_idx=None, topk_w=None, ws=None,
                       stream=None):
     """In place: h <- h + moe(rms_norm(h)).  Returns h."""
+    _check_router(h, Wg)
+    _check_experts(h, W1, W3, W2)
     T, d = h.shape
     E, d_ff, _ = W1.shape
+    if Wg.shape[0] != E:
+        raise ValueError(f"Wg has {Wg.shape[0]} experts, W1 {E}")
+    _check_out("topk_idx", topk_idx, (T, k), torch.int32)
+    _check_out("topk_w", topk_w, (T, k), torch.float32)
     if ws is None:
         ws = workspace(T, d, d_ff, E, k, h.dtype, h.device)
     _call("moe_block_forward", _p(h), _p(Wg), _p(W1), _p(W3), _p(W2), _dt(h), T, d, d_ff, E, k,

@@ -116,3 +116,30 @@ def test_route_balance_workspace_size_rules():
     assert ws(32, 8) >= 32 * 8 * 12
     assert ws(16384, 8) >= 4096 * 8 * 12
     assert ws(16384, 8) > ws(4096, 8) > 0
+
+
+def test_binding_rejects_mismatched_tensors_before_the_call():
+    """The binding checks dtypes and shapes on the host: a bf16 gate matrix or
+    experts of another width would otherwise be read past their ends."""
+    import torch
+
+    T, d, d_ff, E = 4, 64, 128, 8
+    x = torch.zeros((T, d), dtype=torch.bfloat16)
+    Wg = torch.zeros((E, d), dtype=torch.float32)
+    W1 = torch.zeros((E, d_ff, d), dtype=torch.bfloat16)
+    W2 = torch.zeros((E, d, d_ff), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="fp32"):
+        moe.moe_route(x, Wg.to(torch.bfloat16), 2)
+    with pytest.raises(ValueError, match="Wg"):
+        moe.moe_route(x, torch.zeros((E, d + 64)), 2)
+    with pytest.raises(TypeError, match="W1"):
+        moe.moe_forward(x, Wg, W1.float(), W1, W2, 2)
+    with pytest.raises(ValueError, match="expert shapes"):
+        moe.moe_forward(x, Wg, W1, W1, W1, 2)
+    with pytest.raises(ValueError, match="experts"):
+        moe.moe_forward(x, Wg[:4], W1, W1, W2, 2)
+    with pytest.raises(ValueError, match="topk_idx"):
+        moe.moe_route(x, Wg, 2, topk_idx=torch.zeros((T, 3), dtype=torch.int32))
+    # well-formed host tensors pass the checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        moe.moe_forward(x, Wg, W1, W1, W2, 2)

@@ -323,6 +323,42 @@ def test_rmsnorm_closed_form_and_torch():
     np.testing.assert_allclose(oracle.rmsnorm(h, 1e-5), ref, rtol=1e-13)
 
 
+@pytest.mark.parametrize("d", [128, 4096])
+def test_rmsnorm_rows_against_torch(d):
+    """orc_rmsnorm_rows over rows of very different scale (eps = 1e-5 dominates
+    the small ones): without rounding it equals torch's fp64 rms_norm row by
+    row (pins the row stride and the per-row mean), with rounding it equals
+    torch's bf16 conversion of that result.  torch converts fp64 to bf16
+    through fp32, which differs from one direct rounding only where the fp32
+    value falls exactly halfway between two bf16 neighbours; there the oracle
+    must hold the neighbour nearer to the fp64 value."""
+    rng = np.random.default_rng(d)
+    scales = np.array([1e-30, 1e-4, 1e-3, 3e-3, 0.1, 1.0, 7.0, 1e3, 1e30])
+    h = rng.standard_normal((len(scales) * 3, d)) * np.repeat(scales, 3)[:, None]
+    eps = float(np.float32(1e-5))
+    want = F.rms_norm(torch.from_numpy(h), (d,), eps=eps).numpy()
+    got = oracle.rmsnorm_rows(h, eps, round_bf16=False)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=0)
+    # the tiny rows are eps-dominated, the large ones are not
+    assert np.abs(got[:3]).max() < 1e-20 and 0.5 < np.abs(got[-3:]).std() < 2
+    got_r = oracle.rmsnorm_rows(h, eps, round_bf16=True)
+    want_r = torch.from_numpy(want).to(torch.bfloat16).double().numpy()
+    diff = got_r != want_r
+    f32 = want.astype(np.float32).astype(np.float64)
+    halfway = torch.from_numpy(f32).to(torch.bfloat16).double().numpy()
+    # an fp32 value halfway between bf16 neighbours has its low 16 bits 0x8000
+    bits = want.astype(np.float32).view(np.uint32)
+    tie = (bits & 0xFFFF) == 0x8000
+    assert (diff <= tie).all(), np.argwhere(diff & ~tie)[:5]
+    if diff.any():
+        lo = np.minimum(got_r[diff], halfway[diff])
+        hi = np.maximum(got_r[diff], halfway[diff])
+        v = want[diff]
+        assert ((lo <= v) & (v <= hi)).all()
+        assert (np.abs(got_r[diff] - v) <= np.abs(halfway[diff] - v)).all()
+    assert (got_r != got).any()  # the rounding flag is honoured
+
+
 def test_block_step_is_residual_over_normalised_moe():
     """h <- bf16(h + moe(bf16(rms_norm(h)))), assembled from torch's rms_norm,
     torch's bf16 conversion and the (separately pinned) layer."""
