@@ -165,6 +165,23 @@ moe_status moe_forward(const void *x, const float *Wg, const void *W1, const voi
                        const void *W2, moe_dtype dt, int64_t T, int d, int d_ff, int E, int k,
                        void *y, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_forward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer, the same kernels and bit-identical results, with the workspace
+ * replaced by a static device array inside the library of
+ * moe_forward_noalloc_max_scratch() bytes (32 MiB; each GPU holds its own
+ * copy from the first call on it until the process ends).  The caller still
+ * passes x, the weights and y.  Shapes whose workspace,
+ * moe_workspace_size(...), exceeds the array return MOE_ERR_WORKSPACE
+ * before anything is enqueued (for d = 4096, d_ff = 14336, E = 8, k = 2 the
+ * limit is T = 195).  The call allocates and frees nothing.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. */
+size_t moe_forward_noalloc_max_scratch(void);
+moe_status moe_forward_noalloc(const void *x, const float *Wg, const void *W1, const void *W3,
+                               const void *W2, moe_dtype dt, int64_t T, int d, int d_ff, int E,
+                               int k, void *y, void *stream);
+
 /* moe_forward with stage markers, for measurement.  `events` points to 6
  * hipEvent_t handles (passed as void*, created by the caller; any entry may
  * be NULL).  events[i] is recorded on `stream` just before stage i is

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "common.h"
 
@@ -310,6 +312,75 @@ moe_status moe_forward(const void *x, const float *Wg, const void *W1, const voi
     if (!ws || ws_bytes < c.total)
         return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, c.total);
     REQUIRE_PTR(ws, kAlign);
+    return forward_impl(x, Wg, W1, W3, W2, dt, T, d, d_ff, E, k, nullptr, y, nullptr, nullptr,
+                        ws, c, nullptr, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---- the layer without a caller workspace ---------------------------------
+//
+// The fused layer's scratch (routing, grouping, SwiGLU rows, expert outputs,
+// K-chunk partial sums) lives in one file-scope device array instead of a
+// caller workspace.  Each GPU holds its own copy from the first call on it
+// until the process ends.  The array's name is a host-side stand-in in host
+// code: its device address comes from hipGetSymbolAddress, once per device,
+// and only that address is passed to kernels.  Nothing in it has to start at
+// zero: every kernel of the layer writes what a later kernel of the same call
+// reads.  Calls that overlap on one GPU share the array and race.
+static constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+moe_status static_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned(p, kAlign))
+            return fail(MOE_ERR_HIP, "scratch array at %p is not %zu-byte aligned", p, kAlign);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_forward_noalloc_max_scratch(void) { return kStaticScratchBytes; }
+
+moe_status moe_forward_noalloc(const void *x, const float *Wg, const void *W1, const void *W3,
+                               const void *W2, moe_dtype dt, int64_t T, int d, int d_ff, int E,
+                               int k, void *y, void *stream) {
+    CHECK(check_shape(T, d, d_ff, E, k, dt, true));
+    if (T == 0) return ok();
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(Wg, 16);
+    REQUIRE_PTR(W1, 16);
+    REQUIRE_PTR(W3, 16);
+    REQUIRE_PTR(W2, 16);
+    REQUIRE_PTR(y, 16);
+    const Carve c = carve(T, d, d_ff, E, k, dt);
+    if (c.total > kStaticScratchBytes)
+        return fail(MOE_ERR_WORKSPACE,
+                    "this shape needs %zu bytes of scratch; the library's static array holds "
+                    "%zu (use moe_forward with a workspace)",
+                    c.total, kStaticScratchBytes);
+    void *ws = nullptr;
+    CHECK(static_scratch(&ws));
     return forward_impl(x, Wg, W1, W3, W2, dt, T, d, d_ff, E, k, nullptr, y, nullptr, nullptr,
                         ws, c, nullptr, (hipStream_t)stream);
 }

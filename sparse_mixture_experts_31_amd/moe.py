@@ -45,6 +45,8 @@ def lib():
         L.moe_last_error.argtypes = []
         L.moe_workspace_size.restype = sz
         L.moe_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+        L.moe_forward_noalloc_max_scratch.restype = sz
+        L.moe_forward_noalloc_max_scratch.argtypes = []
         L.moe_expert_ffn_kernels.restype = ctypes.c_char_p
         L.moe_expert_ffn_kernels.argtypes = [i64, i32, i32, i32, i32, i32]
         L.moe_route_balance_workspace_size.restype = sz
@@ -57,6 +59,7 @@ def lib():
             "moe_combine": [P, P, P, P, i32, i64, i32, i32, P, P],
             "moe_forward": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, sz, P],
             "moe_forward_profiled": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, sz, P, P],
+            "moe_forward_noalloc": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P],
             "moe_rmsnorm": [P, i32, i64, i32, f32, P, P],
             "moe_block_forward": [P, P, P, P, P, i32, i64, i32, i32, i32, i32, f32, P, P, P, sz,
                                   P],
@@ -260,6 +263,23 @@ def moe_forward(x, Wg, W1, W3, W2, k, y=None, ws=None, stream=None):
         ws = workspace(T, d, d_ff, E, k, x.dtype, x.device)
     _call("moe_forward", _p(x), _p(Wg), _p(W1), _p(W3), _p(W2), _dt(x), T, d, d_ff, E, k, _p(y),
           _p(ws), ws.numel(), _s(stream))
+    return y
+
+
+def moe_forward_noalloc(x, Wg, W1, W3, W2, k, y=None, stream=None):
+    """The layer on the library's static scratch array: no workspace argument.
+    (The C call allocates nothing; pass y to avoid torch allocating it.)"""
+    _check_router(x, Wg)
+    _check_experts(x, W1, W3, W2)
+    T, d = x.shape
+    E, d_ff, _ = W1.shape
+    if Wg.shape[0] != E:
+        raise ValueError(f"Wg has {Wg.shape[0]} experts, W1 {E}")
+    _check_out("y", y, (T, d), x.dtype)
+    if y is None:
+        y = torch.empty_like(x)
+    _call("moe_forward_noalloc", _p(x), _p(Wg), _p(W1), _p(W3), _p(W2), _dt(x), T, d, d_ff, E,
+          k, _p(y), _s(stream))
     return y
 
 

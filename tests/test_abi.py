@@ -143,3 +143,24 @@ def test_binding_rejects_mismatched_tensors_before_the_call():
     # well-formed host tensors pass the checks and stop at the device check
     with pytest.raises(ValueError, match="GPU"):
         moe.moe_forward(x, Wg, W1, W1, W2, 2)
+
+
+def test_noalloc_entry_point_rejects_shapes_beyond_its_array():
+    """moe_forward_noalloc works inside the library's fixed static array:
+    shapes whose workspace exceeds it are refused before anything else
+    happens (no device is touched), smaller ones pass this check."""
+    L = moe.lib()
+    cap = L.moe_forward_noalloc_max_scratch()
+    assert cap == 32 << 20
+    ws = moe.moe_workspace_size
+    assert ws(195, 4096, 14336, 8, 2, moe.MOE_BF16) <= cap < ws(196, 4096, 14336, 8, 2,
+                                                               moe.MOE_BF16)
+
+    def call(T):
+        return L.moe_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, moe.MOE_BF16, T, 4096, 14336,
+                                     8, 2, FAKE, None)
+
+    assert call(196) == moe.MOE_ERR_WORKSPACE
+    assert "static array" in L.moe_last_error().decode()
+    assert call(-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(0) == moe.MOE_OK
