@@ -76,7 +76,7 @@ size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace segments of the fused calls, in order.
 struct Carve {
-    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, split, total;
+    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, split, ctr, total;
     size_t split_bytes;
 };
 
@@ -96,6 +96,7 @@ Carve carve(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt) {
     c.xn = o;       o += up((size_t)T * d * es);
     c.split_bytes = moe_expert_ffn_scratch_bytes((int)dt, (int64_t)A, d, d_ff, E);
     c.split = o;    o += up(c.split_bytes);  // partial sums of K-split expert tiles
+    c.ctr = o;      o += up((size_t)moe_stream_combine_counters(d) * 4);  // decode combine
     c.total = o;
     return c;
 }
@@ -275,6 +276,23 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
     LAUNCH(mark(0), "event");
     LAUNCH(moe_launch_router(x, (int)dt, Wg, T, d, E, k, idx, gw, nullptr, s), "router");
     LAUNCH(mark(1), "event");
+    if (moe_expert_ffn_streams((int)dt, A, d, d_ff, E)) {
+        // Decode sizes: the weight-streaming GEMM1 groups the assignments
+        // itself and GEMM2 also combines (dispatch and combine stages empty).
+        LAUNCH(mark(2), "event");
+        LAUNCH(moe_launch_stream_layer(x, idx, k, gw, residual, W1, W3, W2, T, d, d_ff, E, counts,
+                                       offsets, row_of, token_of, at<int32_t>(ws, c.ctr), hbuf,
+                                       (float *)o_perm, y,
+                                       c.split_bytes ? at<char>(ws, c.split) : nullptr,
+                                       c.split_bytes, ev ? (hipEvent_t)ev[3] : nullptr, s),
+               "expert_ffn");
+        LAUNCH(mark(4), "event");
+        if (!moe_stream_combines(A, E))
+            LAUNCH(moe_launch_combine(o_perm, 1, row_of, gw, residual, (int)dt, T, d, k, y, s),
+                   "combine");
+        LAUNCH(mark(5), "event");
+        return ok();
+    }
     LAUNCH(moe_launch_dispatch_index(idx, A, E, k, counts, offsets, row_of, token_of, s),
            "dispatch");
     // The large-tile and weight-streaming expert kernels read each token's

@@ -358,6 +358,40 @@ bool moe_expert_ffn_gathers(int dt, int64_t A, int d, int d_ff, int E) {
     return moe::path_gathers(moe::ffn_path(dt, A, d, d_ff, E));
 }
 
+bool moe_expert_ffn_streams(int dt, int64_t A, int d, int d_ff, int E) {
+    return moe::ffn_path(dt, A, d, d_ff, E) == moe::FfnPath::kStream;
+}
+
+bool moe_stream_combines(int64_t A, int E) { return moe::stream_combines(A, E); }
+
+int moe_stream_combine_counters(int d) { return moe::stream_combine_counters(d); }
+
+hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k, const float *gw,
+                                   const void *residual, const void *W1, const void *W3,
+                                   const void *W2, int64_t T, int d, int d_ff, int E,
+                                   int32_t *counts, int32_t *offsets, int32_t *row_of,
+                                   int32_t *token_of, int32_t *ctr, void *hbuf, float *o_perm,
+                                   void *y, void *scratch, size_t scratch_bytes,
+                                   hipEvent_t gemm1_done, hipStream_t s) {
+    const int64_t A = T * k;
+    moe::StreamFuse f{};
+    f.topk_idx = topk_idx;
+    f.k = k;
+    f.counts = counts;
+    f.offsets = offsets;
+    f.row_of = row_of;
+    f.token_of = token_of;
+    f.ctr = ctr;
+    if (moe::stream_combines(A, E)) {
+        f.gw = gw;
+        f.residual = (const moe::bf16_t *)residual;
+        f.y = (moe::bf16_t *)y;
+        f.T = (int)T;
+    }
+    return moe::launch_stream_fused(x, W1, W3, W2, A, d, d_ff, E, hbuf, o_perm, (float *)scratch,
+                                    scratch_bytes, f, gemm1_done, s);
+}
+
 const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E) {
     switch (moe::ffn_path(dt, A, d, d_ff, E)) {
         case moe::FfnPath::kStream:

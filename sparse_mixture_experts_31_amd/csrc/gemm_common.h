@@ -197,6 +197,29 @@ static inline int device_cus() {
     return cus;
 }
 
+// What the decode path folds into the weight-streaming kernels
+// (stream_gemm.hip), so a layer is three launches: router, GEMM1, GEMM2.
+// All NULL / 0: the kernels run alone.
+struct StreamFuse {
+    // GEMM1 groups the assignments itself (no dispatch launch): topk_idx
+    // [A] holds the expert of every (token, slot), k slots per token; every
+    // workgroup derives the same stable grouping, workgroup 0 writes it out
+    // (counts [E], offsets [E+1], row_of [A], token_of [A]) and zeroes
+    // GEMM2's ctr_n combine counters.
+    const int32_t *topk_idx;
+    int k;
+    int32_t *counts, *offsets, *row_of, *token_of;
+    int32_t *ctr;
+    int ctr_n;
+    // GEMM2 (fp32 expert outputs) combines: the last workgroup to finish a
+    // column block writes y[t] = sum_j gw[t][j] out[row_of[t][j]] (+
+    // residual[t]) for every token t < T on that block's columns.
+    const float *gw;
+    const bf16_t *residual;
+    bf16_t *y;
+    int T;
+};
+
 // Weight-streaming expert GEMMs for decode-sized bf16 batches
 // (stream_gemm.hip).
 // `partial` (may be NULL) is scratch for the K chunks of GEMM2 at the
@@ -208,6 +231,15 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
                              int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
                              float *partial, size_t partial_bytes, hipEvent_t mid,
                              hipStream_t s);
+// The decode layer's experts with the grouping folded into GEMM1 and, when
+// stream_combines(A, E), the combine folded into GEMM2 (out: fp32).  act is
+// x (rows read in place); offsets receives the grouping (fuse.offsets).
+bool stream_combines(int64_t A, int E);
+int stream_combine_counters(int d);
+hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, const void *W2,
+                               int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
+                               float *partial, size_t partial_bytes, const StreamFuse &fuse,
+                               hipEvent_t gemm1_done, hipStream_t s);
 
 // Wide-tile expert GEMMs (wide_gemm.hip), bf16 only.  `partial` (may be
 // NULL) is scratch for split tiles, at least wide_partial_bytes() bytes.

@@ -52,7 +52,7 @@ constexpr int kSTokBuf = kSBT * 1024;
 constexpr int kSMapMax = 33 * 64;  // token_of entries: A < 33 E on this path, E <= 64
 constexpr int kSLds = kSP * kSWStage + 2 * kSTokBuf + kSMapMax * 4;
 constexpr int kSPartHdr = 64;  // floats before the chunk slices (the chosen chunk count)
-static_assert(kSLds <= 160 * 1024 - 1024, "LDS capacity");
+static_assert(kSLds <= 160 * 1024 - 3 * 1024, "LDS capacity (3 KiB of static tables)");
 static_assert(kSGrp == 16 && kSGroups == 8, "one 16-row MFMA fragment per stage, 8 per K range");
 static_assert(kSP - 1 <= kSGroups / 2, "prologue stages carry no token loads");
 
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ gather,
     const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb,
     const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out,
-    int kc_max, float *__restrict__ part) {
+    int kc_max, float *__restrict__ part, const StreamFuse fz) {
     constexpr int P = kSP, G = kSGroups;
     constexpr int kCols = SWIGLU ? kSRowsT / 2 : kSRowsT;  // output columns per tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -86,6 +86,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     char *const tbuf = smem + P * kSWStage;
     int32_t *const s_map = (int32_t *)(smem + P * kSWStage + 2 * kSTokBuf);
     __shared__ int s_lo[64], s_cnt[64], s_first[65];
+    __shared__ int s_goff[65], s_gbase[64], s_gwc[4][64];  // grouping (fz.topk_idx)
+    // Stable grouping of the A assignments by expert, as the dispatch
+    // kernel does it (dispatch.hip), by one workgroup: an LDS histogram and
+    // its scan give every expert's first row; then 256 assignments a round,
+    // a lane's rank among the lanes of its wave with the same expert (one
+    // ballot per expert) plus the earlier waves' and rounds' counts give its
+    // row, so rows inside an expert follow ascending assignment index.  The
+    // experts are staged in `se` (the ring, idle until the prologue); the
+    // map row -> token goes to `map`; workgroup 0 writes the grouping out.
+    auto group_assignments = [&](const StreamFuse &f, int A_, int E_, int32_t *se, int32_t *map) {
+        const int t = threadIdx.x, ln = t & (kWave - 1), wv = t / kWave;
+        const bool writer = blockIdx.x == 0;
+        for (int a = t; a < A_; a += 256) se[a] = f.topk_idx[a];
+        if (t < 64) s_gbase[t] = 0;
+        __syncthreads();
+        for (int a = t; a < A_; a += 256) {
+            const int e = se[a];
+            if ((unsigned)e < (unsigned)E_) atomicAdd(&s_gbase[e], 1);
+        }
+        __syncthreads();
+        if (wv == 0) {
+            const int c = ln < E_ ? s_gbase[ln] : 0;
+            int incl = c;
+#pragma unroll
+            for (int dd = 1; dd < kWave; dd <<= 1) {
+                const int v = __shfl_up(incl, dd);
+                if (ln >= dd) incl += v;
+            }
+            if (ln < E_) {
+                s_goff[ln] = incl - c;
+                s_gbase[ln] = incl - c;
+                if (writer) {
+                    f.counts[ln] = c;
+                    f.offsets[ln] = incl - c;
+                }
+            }
+            if (ln == E_ - 1) {
+                s_goff[E_] = incl;
+                if (writer) f.offsets[E_] = incl;
+            }
+        }
+        if (writer && f.ctr)
+            for (int i = t; i < f.ctr_n; i += 256) f.ctr[i] = 0;
+        __syncthreads();
+        const uint64_t lower = (ln == 0) ? 0ull : (~0ull >> (64 - ln));
+        for (int r0 = 0; r0 < A_; r0 += 256) {
+            const int a = r0 + t;
+            const int e = a < A_ ? se[a] : -1;
+            const bool valid = (unsigned)e < (unsigned)E_;
+            int rank = 0, cnt = 0;
+            for (int ex = 0; ex < E_; ++ex) {
+                const uint64_t m = __ballot(e == ex);
+                if (e == ex) rank = __popcll(m & lower);
+                if (ln == ex) cnt = __popcll(m);
+            }
+            s_gwc[wv][ln] = cnt;
+            __syncthreads();
+            if (valid) {
+                int row = s_gbase[e] + rank;
+                for (int w = 0; w < wv; ++w) row += s_gwc[w][e];
+                map[row] = a / f.k;
+                if (writer) {
+                    f.row_of[a] = row;
+                    f.token_of[row] = a / f.k;
+                }
+            } else if (writer && a < A_) {
+                f.row_of[a] = -1;
+            }
+            __syncthreads();
+            if (t < E_) s_gbase[t] += s_gwc[0][t] + s_gwc[1][t] + s_gwc[2][t] + s_gwc[3][t];
+            __syncthreads();
+        }
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -96,8 +169,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // Per-expert tile table (token tiles fastest, then column tiles) by wave
     // 0; meanwhile the other three copy the token map, four loads in flight
-    // per lane, so the whole set-up is about one memory round trip.
-    if (wave == 0) {
+    // per lane, so the whole set-up is about one memory round trip.  With
+    // fz.topk_idx (GEMM1 of the decode layer) the workgroup first groups the
+    // assignments itself and the table and map come from that.
+    if (SWIGLU && fz.topk_idx) {
+        group_assignments(fz, A, E, (int32_t *)wring, s_map);
+        if (wave == 0) build_expert_table(s_goff, E, A, kSBT, col_tiles, s_lo, s_cnt, s_first);
+    } else if (wave == 0) {
         build_expert_table(offsets, E, A, kSBT, col_tiles, s_lo, s_cnt, s_first);
     } else if (gather) {
         constexpr int kStride = 256 - kWave;
@@ -335,7 +413,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                             r[q] = acc[h][q];
                             if constexpr (SWIGLU) r[q] = silu(r[q]) * acc[h + 2][q];
                         }
-                        store4<TO>(out + row * N + n, r[0], r[1], r[2], r[3]);
+                        if (!SWIGLU && fz.y) {
+                            // read by another workgroup in this launch: written
+                            // through to memory (agent-coherent stores)
+                            uint64_t *p = (uint64_t *)(out + row * N + n);
+                            __hip_atomic_store(p, ((uint64_t)__float_as_uint(r[1]) << 32) |
+                                                      __float_as_uint(r[0]),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            __hip_atomic_store(p + 1, ((uint64_t)__float_as_uint(r[3]) << 32) |
+                                                          __float_as_uint(r[2]),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        } else {
+                            store4<TO>(out + row * N + n, r[0], r[1], r[2], r[3]);
+                        }
                     }
                 }
             }
@@ -344,6 +434,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = 0; i < 4; ++i) acc[i] = f32x4{};
     }
     wait_vmcnt_lgkm0<0>();  // the trailing reloads land before the wave ends
+
+    // The decode layer's combine (GEMM2, fp32 outputs, one K chunk): this
+    // workgroup's tiles are counted in their column blocks; the workgroup
+    // that completes a block (every token tile of every expert on its
+    // columns stored) forms y on those columns for all T tokens.  The
+    // outputs were written through to memory and every wave waited for its
+    // stores (above) before the count, and the completing workgroup reads
+    // them with agent-coherent loads: no cache flush or invalidation (those
+    // stall the other workgroups of the XCD still streaming).
+    if constexpr (!SWIGLU && std::is_same<TO, float>::value) {
+        if (fz.y && kc == 1) {
+            __shared__ int s_done;
+            __syncthreads();
+            const int per_block = tiles / col_tiles;  // token tiles of all experts
+            for (int ck = 0; ck < my_items; ++ck) {
+                const int cb = item_info(ck).ti.n0 / kCols;
+                if (tid == 0)
+                    s_done = __hip_atomic_fetch_add(&fz.ctr[cb], 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) == per_block - 1;
+                __syncthreads();
+                if (s_done) {
+                    constexpr int kC8 = kCols / 8;  // 8-column pieces of a block
+                    for (int q = tid; q < fz.T * kC8; q += 256) {
+                        const int t = q / kC8;
+                        const int n = cb * kCols + (q - t * kC8) * 8;
+                        if (n >= N) continue;
+                        float acc8[8];
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) acc8[c] = 0.f;
+                        for (int j = 0; j < fz.k; ++j) {
+                            const int r = fz.row_of[t * fz.k + j];
+                            if (r < 0) continue;
+                            const float g = fz.gw[t * fz.k + j];
+                            float o[8];
+                            const uint64_t *p = (const uint64_t *)(out + (int64_t)r * N + n);
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const uint64_t v = __hip_atomic_load(p + c, __ATOMIC_RELAXED,
+                                                                     __HIP_MEMORY_SCOPE_AGENT);
+                                o[2 * c] = __uint_as_float((uint32_t)v);
+                                o[2 * c + 1] = __uint_as_float((uint32_t)(v >> 32));
+                            }
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) acc8[c] = fmaf(g, o[c], acc8[c]);
+                        }
+                        if (fz.residual) {
+                            const uint4 rv = *(const uint4 *)(fz.residual + (int64_t)t * N + n);
+                            const uint32_t w4[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                acc8[2 * i] += bf16_bits_to_f32(w4[i] & 0xffffu);
+                                acc8[2 * i + 1] += bf16_bits_to_f32(w4[i] >> 16);
+                            }
+                        }
+                        *(uint4 *)(fz.y + (int64_t)t * N + n) =
+                            make_uint4(pack_bf16x2(acc8[0], acc8[1]), pack_bf16x2(acc8[2], acc8[3]),
+                                       pack_bf16x2(acc8[4], acc8[5]), pack_bf16x2(acc8[6], acc8[7]));
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
 }
 
 // The K chunks' partial sums added in chunk order (so the sum is the same
@@ -392,7 +545,8 @@ int stream_chunk_limit(int64_t A, int E) { return (A > 0 && A < 4 * (int64_t)E) 
 template <bool SWIGLU, typename TO>
 hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
-                         void *out, int kc_max, float *part, hipStream_t s) {
+                         void *out, int kc_max, float *part, hipStream_t s,
+                         const StreamFuse &fz = StreamFuse{}) {
     hipError_t err = set_lds_limit<stream_gemm_kernel<SWIGLU, TO>>(kSLds);
     if (err != hipSuccess) return err;
     // one workgroup per CU, never more than there can be items:
@@ -402,7 +556,7 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather,
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), item_bound));
     hipLaunchKernelGGL((stream_gemm_kernel<SWIGLU, TO>), dim3(grid), dim3(256), kSLds, s,
                        (const bf16_t *)act, act_ld, gather, (const bf16_t *)Wa,
-                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, kc_max, part);
+                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, kc_max, part, fz);
     if ((err = hipGetLastError()) != hipSuccess || kc_max == 1) return err;
     const int64_t n4 = A * N / 4;  // N is a multiple of 512
     const int rgrid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
@@ -425,6 +579,36 @@ bool stream_supported(int64_t A, int d, int d_ff, int E) {
     // whole 1 KiB row pieces, and the token map fits its LDS area
     return d % kSKRange == 0 && d_ff % kSKRange == 0 && d >= kSKRange && d_ff >= kSKRange &&
            A <= kSMapMax && E <= 64;
+}
+
+bool stream_combines(int64_t A, int E) { return stream_chunk_limit(A, E) == 1; }
+
+int stream_combine_counters(int d) { return (d + kSRowsT - 1) / kSRowsT; }
+
+hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, const void *W2,
+                               int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
+                               float *partial, size_t partial_bytes, const StreamFuse &fuse,
+                               hipEvent_t gemm1_done, hipStream_t s) {
+    int kc = stream_chunk_limit(A, E);
+    if (kc > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) kc = 1;
+    // GEMM1 reads token rows through the map it builds; GEMM2's combine only
+    // runs where its tiles hold whole K (one chunk)
+    StreamFuse f1 = fuse;
+    f1.ctr_n = fuse.y && kc == 1 ? stream_combine_counters(d) : 0;
+    f1.gw = nullptr;
+    f1.residual = nullptr;
+    f1.y = nullptr;
+    hipError_t err = launch_stream<true, bf16_t>(x, d, fuse.token_of, W1, W3, fuse.offsets, E,
+                                                 d_ff, d, A, hbuf, kc, partial, s, f1);
+    if (err == hipSuccess && gemm1_done) err = hipEventRecord(gemm1_done, s);
+    if (err != hipSuccess) return err;
+    StreamFuse f2{};
+    if (kc == 1 && fuse.y) {
+        f2 = fuse;
+        f2.topk_idx = nullptr;
+    }
+    return launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, fuse.offsets, E, d, d_ff,
+                                       A, out, kc, partial, s, f2);
 }
 
 hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,

@@ -388,6 +388,21 @@ def test_stack_small():
     _stack_check(w, blocks, h0, np.arange(w.T))
 
 
+@pytest.mark.parametrize("T", [32, 8])
+def test_stack_decode_sized(T):
+    """Decoder blocks at decode sizes run on the weight-streaming kernels,
+    where GEMM1 groups the assignments itself and (from four rows per
+    expert on, T = 32 here) GEMM2 forms h + y in place; T = 8 keeps the
+    separate combine."""
+    from sparse_mixture_experts_31_amd.inputs import make_stack
+    w = Workload(f"stack-decode-{T}", 42, T=T, d=1024, d_ff=2048, blocks=3)
+    assert moe.moe_expert_ffn_kernels(T, w.d, w.d_ff, w.E, w.k, torch.bfloat16) == \
+        "stream_gemm_kernel"
+    log(f"case {w.name}")
+    h0, blocks = make_stack(w, DEV, 0)
+    _stack_check(w, blocks, h0, np.arange(w.T))
+
+
 # ------------------------------------------------------------------ full sizes
 
 
