@@ -465,6 +465,34 @@ def test_full_size_layer(name):
     _forward_and_check(w, L, rows=rows)
 
 
+# ------------------------------------------- kernel-family thresholds, full shape
+
+@pytest.fixture(scope="module")
+def prefill_layer():
+    w = WORKLOADS["prefill"]
+    return w, _case(w)
+
+
+@pytest.mark.parametrize("T,family", [
+    (99, "stream_gemm_kernel"),                      # 24 rows per expert on average
+    (100, "grouped_gemm_kernel (128 x 64 tiles)"),   # 25
+    (195, "grouped_gemm_kernel (128 x 64 tiles)"),   # 48
+    (196, "wide_gemm_kernel (128-row token tiles)"),  # 49
+    (400, "wide_gemm_kernel (128-row token tiles)"),  # 100
+    (401, "wide_gemm_kernel (256-row token tiles)"),  # 100.25
+])
+def test_kernel_family_thresholds_at_the_mixtral_shape(prefill_layer, T, family):
+    """The layer on the full Mixtral shape at the batch sizes where the
+    library switches expert kernels (by the average rows per expert, T k /
+    E), on both sides of every switch: each side must match the oracle."""
+    w0, L0 = prefill_layer
+    w = w0.with_(name=f"threshold-T{T}", T=T)
+    assert moe.moe_expert_ffn_kernels(T, w.d, w.d_ff, w.E, w.k, torch.bfloat16) == family
+    L = dict(L0, x=L0["x"][:T].contiguous())
+    rows = np.union1d(np.random.default_rng(T).choice(T, 40, replace=False), [0, T - 1])
+    _forward_and_check(w, L, rows=rows)
+
+
 # ------------------------------------------------------ decode sweep T = 1..16
 
 @pytest.fixture(scope="module")
