@@ -123,10 +123,15 @@ moe_status moe_route_balance(const void *x, const float *Wg, moe_dtype dt, int64
  * Inside an expert's block rows are in ascending (t, j) order, so the result
  * is unique and deterministic.  Experts may receive no rows.  Entries of
  * topk_idx outside [0, E) are skipped and get row_of = -1.
- * ws: the workspace (at least moe_workspace_size(...) bytes).
+ * ws: at least moe_permute_workspace_size(T, E, k) bytes, 256-byte aligned
+ * (moe_workspace_size(...) bytes are also enough).  That size is 0 up to
+ * 4096 assignments, where one workgroup groups them and ws may be NULL;
+ * larger batches are cut into chunks whose per-expert counts ws holds.
+ * MOE_ERR_WORKSPACE if ws is missing or too small.
  * Defined by: tokentrails lineage, step "Two experts per token" (tokens are
  * sent to their experts; some experts get more of the batch, some none);
  * flashpapers summary "How It Works" (an expert with G_i = 0 is skipped). */
+size_t moe_permute_workspace_size(int64_t T, int E, int k);
 moe_status moe_permute(const void *x, const int32_t *topk_idx, moe_dtype dt, int64_t T, int d,
                        int E, int k, int32_t *counts, int32_t *offsets, int32_t *row_of,
                        int32_t *token_of, void *x_perm, void *ws, size_t ws_bytes,

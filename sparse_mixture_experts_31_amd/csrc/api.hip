@@ -76,7 +76,8 @@ size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace segments of the fused calls, in order.
 struct Carve {
-    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, split, ctr, total;
+    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, split, ctr, dsc,
+        total;
     size_t split_bytes;
 };
 
@@ -97,6 +98,7 @@ Carve carve(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt) {
     c.split_bytes = moe_expert_ffn_scratch_bytes((int)dt, (int64_t)A, d, d_ff, E);
     c.split = o;    o += up(c.split_bytes);  // partial sums of K-split expert tiles
     c.ctr = o;      o += up((size_t)moe_stream_combine_counters(d) * 4);  // decode combine
+    c.dsc = o;      o += up(moe_dispatch_scratch_bytes((int64_t)A, E));  // dispatch chunk counts
     c.total = o;
     return c;
 }
@@ -183,19 +185,23 @@ moe_status moe_route_balance(const void *x, const float *Wg, moe_dtype dt, int64
     return ok();
 }
 
+size_t moe_permute_workspace_size(int64_t T, int E, int k) {
+    if (T < 0 || E < 1 || E > 64 || k < 1 || k > E || k > 8 || T * (int64_t)k >= (1LL << 31))
+        return 0;
+    return moe_dispatch_scratch_bytes(T * k, E);
+}
+
 moe_status moe_permute(const void *x, const int32_t *topk_idx, moe_dtype dt, int64_t T, int d,
                        int E, int k, int32_t *counts, int32_t *offsets, int32_t *row_of,
                        int32_t *token_of, void *x_perm, void *ws, size_t ws_bytes,
                        void *stream) {
-    (void)ws;
-    (void)ws_bytes;  // the single-workgroup dispatch keeps its state in LDS
     CHECK(check_shape(T, d, 64, E, k, dt, false));
     REQUIRE_PTR(counts, 4);
     REQUIRE_PTR(offsets, 4);
     if (T == 0) {
         // still define the (empty) grouping
         LAUNCH(moe_launch_dispatch_index(topk_idx, 0, E, k, counts, offsets, row_of, token_of,
-                                         (hipStream_t)stream),
+                                         nullptr, (hipStream_t)stream),
                "dispatch");
         return ok();
     }
@@ -204,8 +210,15 @@ moe_status moe_permute(const void *x, const int32_t *topk_idx, moe_dtype dt, int
     REQUIRE_PTR(row_of, 4);
     REQUIRE_PTR(token_of, 4);
     REQUIRE_PTR(x_perm, 16);
+    const size_t need = moe_dispatch_scratch_bytes(T * k, E);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+        REQUIRE_PTR(ws, kAlign);
+    }
     hipStream_t s = (hipStream_t)stream;
-    LAUNCH(moe_launch_dispatch_index(topk_idx, T * k, E, k, counts, offsets, row_of, token_of, s),
+    LAUNCH(moe_launch_dispatch_index(topk_idx, T * k, E, k, counts, offsets, row_of, token_of,
+                                     need > 0 ? (int32_t *)ws : nullptr, s),
            "dispatch");
     LAUNCH(moe_launch_gather_rows(x, (int)dt, T, d, k, row_of, x_perm, s), "gather");
     return ok();
@@ -293,7 +306,8 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
         LAUNCH(mark(5), "event");
         return ok();
     }
-    LAUNCH(moe_launch_dispatch_index(idx, A, E, k, counts, offsets, row_of, token_of, s),
+    LAUNCH(moe_launch_dispatch_index(idx, A, E, k, counts, offsets, row_of, token_of,
+                                     at<int32_t>(ws, c.dsc), s),
            "dispatch");
     // The large-tile and weight-streaming expert kernels read each token's
     // row in place through token_of; the others read rows in expert order,

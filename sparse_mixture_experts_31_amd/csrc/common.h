@@ -69,9 +69,13 @@ hipError_t moe_launch_route_balance(const void *x, int dt, const float *Wg, int6
                                     int E, int k, int32_t *idx, float *gw, double *part_p,
                                     int32_t *part_c, float *f, float *P, float *laux,
                                     hipStream_t s);
+// Grouping of A assignments by expert.  `scratch` holds the chunk counts of
+// the two-launch form, at least moe_dispatch_scratch_bytes(A, E) bytes; with
+// NULL (or where that is 0) one workgroup does it all.
+size_t moe_dispatch_scratch_bytes(int64_t A, int E);
 hipError_t moe_launch_dispatch_index(const int32_t *idx, int64_t A, int E, int k,
                                      int32_t *counts, int32_t *offsets, int32_t *row_of,
-                                     int32_t *token_of, hipStream_t s);
+                                     int32_t *token_of, int32_t *scratch, hipStream_t s);
 hipError_t moe_launch_gather_rows(const void *x, int dt, int64_t T, int d, int k,
                                   const int32_t *row_of, void *x_perm, hipStream_t s);
 // Grouped expert GEMMs over activations already in expert order (x_perm).

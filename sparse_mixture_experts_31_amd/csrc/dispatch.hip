@@ -17,8 +17,25 @@
 //      per thread), so a window costs one memory round trip instead of one
 //      per round.  Rows inside an expert's block thus follow ascending
 //      assignment index (t*k + j): a unique, deterministic order.
+// Above 4096 assignments two launches that spread over the chip take over:
+// the single workgroup walks the assignments 1024 at a time, about 1.5 us a
+// round on MI355X (94 us for 32768), while the two launches take 9-11 us of
+// kernel time from 4096 to 32768 assignments.
+// The two launches:
+// dispatch_chunk_rank_kernel: one wave per chunk of W consecutive
+//   assignments; lane e keeps expert e's running count inside the chunk, and
+//   64 assignments at a time one ballot per expert gives a lane its rank
+//   among the chunk's earlier assignments of the same expert.  The rank goes
+//   to row_of (a provisional value), the chunk's E counts to `cnt`.
+// dispatch_place_kernel: every workgroup sums the chunk counts (the totals
+//   give counts and offsets, which workgroup 0 writes; the chunks before its
+//   own give its first row per expert), then each wave turns its chunk's
+//   ranks into rows.  Chunks are in assignment order, so the rows are the
+//   same stable grouping as above.
 // gather_rows_kernel: one wave per token reads the token's row once with
 //   16-byte loads and writes it to each of its k rows of x_perm.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -26,6 +43,7 @@ namespace moe {
 constexpr int kDispatchThreads = 1024;
 constexpr int kDispatchWaves = kDispatchThreads / kWave;
 constexpr int kDispatchWindow = 8192;  // indices staged in LDS at a time
+constexpr int64_t kDispatchChunkedFrom = 4096;  // larger batches: the two-launch form
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
 // every global store of the wave to complete, which here would stall each
@@ -133,6 +151,130 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_index_kernel(
     }
 }
 
+constexpr int kChunkWaves = 4;   // chunks (one wave each) per workgroup
+constexpr int kChunkBatch = 4;   // index loads in flight per lane
+
+__global__ __launch_bounds__(kChunkWaves * kWave) void dispatch_chunk_rank_kernel(
+    const int32_t *__restrict__ idx, int A, int E, int W, int nch, int32_t *__restrict__ row_of,
+    int32_t *__restrict__ cnt) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ch = blockIdx.x * kChunkWaves + (int)threadIdx.x / kWave;
+    if (ch >= nch) return;  // uniform over the wave
+    const int64_t a0 = (int64_t)ch * W, a1 = min((int64_t)A, a0 + W);
+    const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int run = 0;  // lane e: assignments of expert e so far in this chunk
+    for (int64_t b = a0; b < a1; b += kChunkBatch * kWave) {
+        int ev[kChunkBatch];
+#pragma unroll
+        for (int q = 0; q < kChunkBatch; ++q) {
+            const int64_t a = b + q * kWave + lane;
+            ev[q] = (a < a1) ? idx[a] : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < kChunkBatch; ++q) {
+            const int64_t a = b + q * kWave + lane;
+            const int e = ev[q];
+            const bool valid = (unsigned)e < (unsigned)E;
+            const int before = __shfl(run, valid ? e : 0);
+            int rank = 0;
+            for (int ex = 0; ex < E; ++ex) {
+                const uint64_t m = __ballot(e == ex);
+                if (e == ex) rank = __popcll(m & lower_lanes);
+                if (lane == ex) run += __popcll(m);
+            }
+            if (a < a1) row_of[a] = valid ? before + rank : -1;
+        }
+    }
+    if (lane < E) cnt[(int64_t)ch * E + lane] = run;
+}
+
+__global__ __launch_bounds__(kChunkWaves * kWave) void dispatch_place_kernel(
+    const int32_t *__restrict__ idx, int A, int E, int k, int W, int nch,
+    const int32_t *__restrict__ cnt, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ row_of, int32_t *__restrict__ token_of) {
+    __shared__ int s_tot[kChunkWaves * kWave], s_pre[kChunkWaves * kWave];
+    __shared__ int s_first[64];  // first row of expert e for this workgroup's first chunk
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int ch0 = blockIdx.x * kChunkWaves;
+    // Sums over the chunk counts: lane l takes expert l % E of the chunks
+    // j, j + J, ... with j = wave * G + l / E (G lane groups per wave).
+    const int G = kWave / E, J = kChunkWaves * G;
+    int tot = 0, pre = 0;
+    if (lane < G * E) {
+        const int e = lane % E;
+        for (int ch = wave * G + lane / E; ch < nch; ch += J) {
+            const int c = cnt[(int64_t)ch * E + e];
+            tot += c;
+            if (ch < ch0) pre += c;
+        }
+    }
+    s_tot[tid] = tot;
+    s_pre[tid] = pre;
+    __syncthreads();
+    if (wave == 0) {
+        int t = 0, p = 0;
+        if (lane < E)
+            for (int w = 0; w < kChunkWaves; ++w)
+                for (int g = 0; g < G; ++g) {
+                    t += s_tot[w * kWave + g * E + lane];
+                    p += s_pre[w * kWave + g * E + lane];
+                }
+        int incl = t;
+#pragma unroll
+        for (int dd = 1; dd < kWave; dd <<= 1) {
+            const int v = __shfl_up(incl, dd);
+            if (lane >= dd) incl += v;
+        }
+        if (lane < E) {
+            s_first[lane] = incl - t + p;
+            if (blockIdx.x == 0) {
+                counts[lane] = t;
+                offsets[lane] = incl - t;
+            }
+        }
+        if (blockIdx.x == 0 && lane == E - 1) offsets[E] = incl;
+    }
+    __syncthreads();
+    const int ch = ch0 + wave;
+    if (ch >= nch) return;  // uniform over the wave
+    // this chunk's first row per expert: the workgroup's, plus the earlier
+    // chunks of the workgroup
+    int first = 0;
+    if (lane < E) {
+        first = s_first[lane];
+        for (int w = 0; w < wave; ++w) first += cnt[(int64_t)(ch0 + w) * E + lane];
+    }
+    const int64_t a0 = (int64_t)ch * W, a1 = min((int64_t)A, a0 + W);
+    for (int64_t b = a0; b < a1; b += kChunkBatch * kWave) {
+        int ev[kChunkBatch], rv[kChunkBatch];
+#pragma unroll
+        for (int q = 0; q < kChunkBatch; ++q) {
+            const int64_t a = b + q * kWave + lane;
+            ev[q] = (a < a1) ? idx[a] : -1;
+            rv[q] = (a < a1) ? row_of[a] : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < kChunkBatch; ++q) {
+            const int64_t a = b + q * kWave + lane;
+            const bool valid = (unsigned)ev[q] < (unsigned)E;
+            const int f = __shfl(first, valid ? ev[q] : 0);
+            if (valid) {
+                const int row = f + rv[q];
+                row_of[a] = row;
+                token_of[row] = (int32_t)(a / k);
+            }
+        }
+    }
+}
+
+// Assignments per chunk of the two-launch dispatch (a multiple of the wave,
+// at most 512 chunks), or 0 where the single workgroup is used.
+int dispatch_chunk_size(int64_t A) {
+    if (A <= kDispatchChunkedFrom) return 0;
+    const int64_t per = (A + 511) / 512;
+    return (int)std::max<int64_t>(256, (per + kWave - 1) / kWave * kWave);
+}
+
 constexpr int kGatherWaves = 4;
 
 __global__ __launch_bounds__(kGatherWaves * kWave) void gather_rows_kernel(
@@ -155,11 +297,30 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_rows_kernel(
 
 }  // namespace moe
 
+size_t moe_dispatch_scratch_bytes(int64_t A, int E) {
+    const int W = moe::dispatch_chunk_size(A);
+    if (W == 0) return 0;
+    return sizeof(int32_t) * (size_t)((A + W - 1) / W) * (size_t)E;
+}
+
 hipError_t moe_launch_dispatch_index(const int32_t *idx, int64_t A, int E, int k,
                                      int32_t *counts, int32_t *offsets, int32_t *row_of,
-                                     int32_t *token_of, hipStream_t s) {
-    hipLaunchKernelGGL(moe::dispatch_index_kernel, dim3(1), dim3(moe::kDispatchThreads), 0, s,
-                       idx, (int)A, E, k, counts, offsets, row_of, token_of);
+                                     int32_t *token_of, int32_t *scratch, hipStream_t s) {
+    const int W = moe::dispatch_chunk_size(A);
+    if (W == 0 || !scratch) {
+        hipLaunchKernelGGL(moe::dispatch_index_kernel, dim3(1), dim3(moe::kDispatchThreads), 0,
+                           s, idx, (int)A, E, k, counts, offsets, row_of, token_of);
+        return hipGetLastError();
+    }
+    const int nch = (int)((A + W - 1) / W);
+    const dim3 grid((unsigned)((nch + moe::kChunkWaves - 1) / moe::kChunkWaves));
+    const dim3 block(moe::kChunkWaves * moe::kWave);
+    hipLaunchKernelGGL(moe::dispatch_chunk_rank_kernel, grid, block, 0, s, idx, (int)A, E, W, nch,
+                       row_of, scratch);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(moe::dispatch_place_kernel, grid, block, 0, s, idx, (int)A, E, k, W, nch,
+                       (const int32_t *)scratch, counts, offsets, row_of, token_of);
     return hipGetLastError();
 }
 

@@ -51,6 +51,8 @@ def lib():
         L.moe_expert_ffn_kernels.argtypes = [i64, i32, i32, i32, i32, i32]
         L.moe_route_balance_workspace_size.restype = sz
         L.moe_route_balance_workspace_size.argtypes = [i64, i32]
+        L.moe_permute_workspace_size.restype = sz
+        L.moe_permute_workspace_size.argtypes = [i64, i32, i32]
         sigs = {
             "moe_route": [P, P, i32, i64, i32, i32, i32, P, P, P, P],
             "moe_route_balance": [P, P, i32, i64, i32, i32, i32, P, P, P, P, P, P, sz, P],
@@ -170,6 +172,10 @@ def moe_route(x, Wg, k, topk_idx=None, topk_w=None, logits=None, stream=None):
     return topk_idx, topk_w
 
 
+def moe_permute_workspace_size(T, E, k) -> int:
+    return int(lib().moe_permute_workspace_size(T, E, k))
+
+
 def moe_route_balance_workspace_size(T, E) -> int:
     return int(lib().moe_route_balance_workspace_size(T, E))
 
@@ -215,8 +221,10 @@ def moe_permute(x, topk_idx, E, counts=None, offsets=None, row_of=None, token_of
     row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
     token_of = torch.empty(T * k, dtype=torch.int32, device=dev) if token_of is None else token_of
     x_perm = torch.empty((T * k, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    n = moe_permute_workspace_size(T, E, k)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
     _call("moe_permute", _p(x), _p(topk_idx), _dt(x), T, d, E, k, _p(counts), _p(offsets),
-          _p(row_of), _p(token_of), _p(x_perm), None, 0, _s(stream))
+          _p(row_of), _p(token_of), _p(x_perm), _p(ws), n, _s(stream))
     return dict(counts=counts, offsets=offsets, row_of=row_of, token_of=token_of, x_perm=x_perm)
 
 

@@ -198,6 +198,62 @@ def test_permute_empty_and_skewed_groups():
     assert to_np(P0["offsets"]).tolist() == [0] * (E + 1)
 
 
+def _stable_grouping(idx, E):
+    """Rows of the valid assignments in expert order, ties in assignment
+    order (a stable sort by expert); entries outside [0, E) get row -1."""
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    order = np.flatnonzero(valid)[np.argsort(flat[valid], kind="stable")]
+    row_of = np.full(flat.shape, -1, np.int32)
+    row_of[order] = np.arange(order.size, dtype=np.int32)
+    return counts, offsets, row_of.reshape(idx.shape), (order // idx.shape[1]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,bad", [
+    (2048, 8, 2, False),     # 4096 assignments: the single-workgroup form
+    (2049, 8, 2, False),     # 4098: the chunked form, a 2-assignment last chunk
+    (700, 13, 3, True),      # single workgroup, out-of-range entries
+    (1400, 13, 3, True),     # chunked, E = 13 (lane groups of 13), out-of-range entries
+    (5000, 1, 1, False),     # one expert
+    (3000, 64, 8, True),     # E = 64: one lane per expert
+    (150000, 8, 2, False),   # 300000 assignments: 640 per chunk, 469 chunks
+])
+def test_permute_both_dispatch_forms(T, E, k, bad):
+    rng = np.random.default_rng(T + E + k)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(min(T, 4096))])
+    idx = np.resize(idx, (T, k)).astype(np.int32)
+    if E > 1:
+        # skew: a quarter of the tokens send their first choice to expert
+        # E - 1 (a slot that held E - 1 takes the old first choice instead)
+        sel = np.flatnonzero(rng.random(T) < 0.25)
+        for j in range(1, k):
+            hit = sel[idx[sel, j] == E - 1]
+            idx[hit, j] = idx[hit, 0]
+        idx[sel, 0] = E - 1
+    if bad:
+        idx.reshape(-1)[rng.choice(T * k, T * k // 50, replace=False)] = \
+            rng.choice([-1, E, 1 << 30, -(1 << 30)], T * k // 50)
+    need = moe.moe_permute_workspace_size(T, E, k)
+    assert (need == 0) == (T * k <= 4096)
+    x = torch.randn((T, 64), device=DEV).to(torch.bfloat16)
+    P = moe.moe_permute(x, torch.from_numpy(idx).to(DEV), E)
+    torch.cuda.synchronize()
+    counts, offsets, row_of, token_of = _stable_grouping(idx, E)
+    if not bad:
+        want = oracle.permute(idx, E)
+        np.testing.assert_array_equal(want["row_of"], row_of)
+    np.testing.assert_array_equal(to_np(P["counts"]), counts)
+    np.testing.assert_array_equal(to_np(P["offsets"]), offsets)
+    np.testing.assert_array_equal(to_np(P["row_of"]), row_of)
+    n = int(offsets[-1])
+    np.testing.assert_array_equal(to_np(P["token_of"])[:n], token_of)
+    # every placed row holds its token's row of x
+    xp = P["x_perm"][:n].cpu()
+    assert torch.equal(xp, x.cpu()[torch.from_numpy(token_of).long()])
+
+
 def test_pieces_expert_ffn_and_combine():
     """moe_expert_ffn and moe_combine on their own, fed from the oracle's grouping."""
     w = Workload("mid-bf16", 10, T=300, d=512, d_ff=1024)
