@@ -300,9 +300,6 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
                                        c.split_bytes, ev ? (hipEvent_t)ev[3] : nullptr, s),
                "expert_ffn");
         LAUNCH(mark(4), "event");
-        if (!moe_stream_combines(A, E))
-            LAUNCH(moe_launch_combine(o_perm, 1, row_of, gw, residual, (int)dt, T, d, k, y, s),
-                   "combine");
         LAUNCH(mark(5), "event");
         return ok();
     }

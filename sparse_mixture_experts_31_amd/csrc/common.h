@@ -93,14 +93,13 @@ hipError_t moe_launch_expert_ffn(const void *act, const int32_t *gather, const i
                                  hipEvent_t mid_event, hipStream_t s);
 bool moe_expert_ffn_gathers(int dt, int64_t A, int d, int d_ff, int E);
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E);
-// The decode layer on the weight-streaming kernels in two launches
+// The decode layer's experts on the weight-streaming kernels
 // (moe_expert_ffn_streams()): GEMM1 groups the assignments itself (topk_idx,
-// k slots per token; counts, offsets, row_of, token_of written out) and, when
-// moe_stream_combines(T k, E), GEMM2 also writes y = sum_j gw o_j (+
-// residual) (bf16; ctr: moe_stream_combine_counters(d) ints of scratch);
-// otherwise o_perm (fp32) is left for moe_launch_combine.
+// k slots per token; counts, offsets, row_of, token_of written out), and
+// GEMM2 (or, where its tiles may be split, the pass that sums their pieces)
+// also writes y = sum_j gw o_j (+ residual) (bf16; o_perm fp32 in between;
+// ctr: moe_stream_combine_counters(d) ints of scratch).
 bool moe_expert_ffn_streams(int dt, int64_t A, int d, int d_ff, int E);
-bool moe_stream_combines(int64_t A, int E);
 int moe_stream_combine_counters(int d);
 hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k, const float *gw,
                                    const void *residual, const void *W1, const void *W3,

@@ -362,8 +362,6 @@ bool moe_expert_ffn_streams(int dt, int64_t A, int d, int d_ff, int E) {
     return moe::ffn_path(dt, A, d, d_ff, E) == moe::FfnPath::kStream;
 }
 
-bool moe_stream_combines(int64_t A, int E) { return moe::stream_combines(A, E); }
-
 int moe_stream_combine_counters(int d) { return moe::stream_combine_counters(d); }
 
 hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k, const float *gw,
@@ -382,12 +380,10 @@ hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k
     f.row_of = row_of;
     f.token_of = token_of;
     f.ctr = ctr;
-    if (moe::stream_combines(A, E)) {
-        f.gw = gw;
-        f.residual = (const moe::bf16_t *)residual;
-        f.y = (moe::bf16_t *)y;
-        f.T = (int)T;
-    }
+    f.gw = gw;
+    f.residual = (const moe::bf16_t *)residual;
+    f.y = (moe::bf16_t *)y;
+    f.T = (int)T;
     return moe::launch_stream_fused(x, W1, W3, W2, A, d, d_ff, E, hbuf, o_perm, (float *)scratch,
                                     scratch_bytes, f, gemm1_done, s);
 }

@@ -222,7 +222,7 @@ struct StreamFuse {
 
 // Weight-streaming expert GEMMs for decode-sized bf16 batches
 // (stream_gemm.hip).
-// `partial` (may be NULL) is scratch for the K chunks of GEMM2 at the
+// `partial` (may be NULL) is scratch for the pieces of split tiles at the
 // smallest batches, at least stream_partial_bytes() bytes (0: none used).
 bool stream_supported(int64_t A, int d, int d_ff, int E);
 size_t stream_partial_bytes(int64_t A, int d, int d_ff, int E);
@@ -231,10 +231,9 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
                              int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
                              float *partial, size_t partial_bytes, hipEvent_t mid,
                              hipStream_t s);
-// The decode layer's experts with the grouping folded into GEMM1 and, when
-// stream_combines(A, E), the combine folded into GEMM2 (out: fp32).  act is
-// x (rows read in place); offsets receives the grouping (fuse.offsets).
-bool stream_combines(int64_t A, int E);
+// The decode layer's experts with the grouping folded into GEMM1 and the
+// combine into GEMM2 or the pass after it (out: fp32 expert outputs).  act
+// is x (rows read in place); offsets receives the grouping (fuse.offsets).
 int stream_combine_counters(int d);
 hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, const void *W2,
                                int64_t A, int d, int d_ff, int E, void *hbuf, float *out,

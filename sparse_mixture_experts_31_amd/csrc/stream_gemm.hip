@@ -190,38 +190,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     __syncthreads();
     auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-    // Work items: tile t's K ranges cut into kc contiguous chunks; item
-    // w = kc t + chunk, taken round robin.  With few tiles (small batches)
-    // whole tiles leave CUs idle for much of the kernel: kc is then 4 when
-    // that finishes at least 10 % sooner in units of whole tiles,
-    // ceil(4 tiles / grid) / 4 against ceil(tiles / grid), else 1.  (Two
-    // chunks measured slower than both one and four on MI355X -- by 10 %
-    // at T = 8, where the count predicted a 7 % gain -- and the chunks'
-    // partial sums and extra pass cost a few percent, hence the margin.)
-    // The same choice in every workgroup, recorded for stream_reduce_kernel.
+    // Work split.  Whole tiles, workgroup b taking the run of tiles
+    // [b tiles / NG, (b + 1) tiles / NG) (a run of neighbouring column tiles
+    // of one expert streams 3 % faster on MI355X than tiles dealt round
+    // robin); or, allowed at the smallest batches (kc_max > 1) where a few
+    // tiles leave CUs idle for much of the kernel, an even split of all
+    // R = tiles x n_kr K ranges in tile order: workgroup b of the NGe used
+    // walks ranges [b R / NGe, (b + 1) R / NGe), cut at tile boundaries into
+    // items.  A tile's pieces (at most kc_max: NGe is kept small enough that
+    // every workgroup gets at least (n_kr - 1) / (kc_max - 1) ranges) leave
+    // fp32 partial sums, summed in K order by stream_reduce_kernel.  The
+    // split is taken when it cuts the K ranges of the busiest workgroup by
+    // at least 10 % (the partial sums and the extra pass cost a few
+    // percent).  Every workgroup makes the same choice; it is recorded in
+    // the header of `part` for the reduce pass.
     const int NG = gridDim.x;
     const int tiles = u(s_first[E]);
-    int kc = 1;
-    if (kc_max >= 4 && n_kr >= 4 &&
-        10 * (int64_t)((tiles * 4 + NG - 1) / NG) < 36 * (int64_t)((tiles + NG - 1) / NG))
-        kc = 4;
-    if (kc_max > 1 && blockIdx.x == 0 && tid == 0) *(int *)part = kc;
+    const int64_t R = (int64_t)tiles * n_kr;
+    bool split = false;
+    int NGe = NG;
+    if (kc_max > 1 && tiles > 0) {
+        const int s_need = n_kr > 1 ? (n_kr - 2) / (kc_max - 1) + 1 : 1;
+        NGe = (int)max<int64_t>(1, min<int64_t>(NG, R / s_need));
+        const int64_t whole = (int64_t)((tiles + NG - 1) / NG) * n_kr;
+        split = 10 * ((R + NGe - 1) / NGe) <= 9 * whole;
+        if (!split) NGe = NG;
+    }
+    if (kc_max > 1 && blockIdx.x == 0 && tid == 0) *(int *)part = split ? kc_max : 1;
     float *const slices = part + kSPartHdr;
-    const int total = tiles * kc;
-    const int my_items = (total > (int)blockIdx.x) ? (total - (int)blockIdx.x + NG - 1) / NG : 0;
+    // pieces of the tile holding (row r, column tile c) at [r * col_tiles + c]
+    int32_t *const np_of =
+        split ? (int32_t *)(slices + (int64_t)kc_max * A * ((SWIGLU ? 2 : 1) * N)) : nullptr;
+    // (R < 2^31: tiles <= 33 x 224 x 64 experts, n_kr <= K / 512)
+    const int g0 = split ? (int)((int64_t)blockIdx.x * R / NGe) : 0;
+    const int g1 = split ? (int)(((int64_t)blockIdx.x + 1) * R / NGe) : 0;
+    const int t_first = g0 / n_kr;
+    int my_items = 0;
+    if (split)
+        my_items = ((int)blockIdx.x < NGe) ? (g1 - 1) / n_kr - t_first + 1 : 0;
+    const int tw0 = (int)((int64_t)blockIdx.x * tiles / NG);
+    const int tw1 = (int)(((int64_t)blockIdx.x + 1) * tiles / NG);
+    if (!split)
+        my_items = tw1 - tw0;
     if (my_items == 0) return;  // uniform over the workgroup
+    // workgroup whose ranges hold global K range g
+    auto wg_of = [&](int g) { return (int)((((int64_t)g + 1) * NGe - 1) / R); };
 
     struct Item {
         TileInfo ti;
-        int kr0, kr1, chunk;  // K ranges [kr0, kr1) of the tile
+        int kr0, kr1;  // K ranges [kr0, kr1) of the tile
+        int t;         // the tile
     };
     auto item_info = [&](int k) {
-        const int w = (int)blockIdx.x + k * NG;
-        const int t = w / kc;
         Item it;
-        it.chunk = w - t * kc;
-        it.kr0 = it.chunk * n_kr / kc;
-        it.kr1 = (it.chunk + 1) * n_kr / kc;
+        int t;
+        if (split) {
+            t = t_first + k;
+            const int t0 = t * n_kr;
+            it.kr0 = max(g0, t0) - t0;
+            it.kr1 = min(g1, t0 + n_kr) - t0;
+        } else {
+            t = tw0 + k;
+            it.kr0 = 0;
+            it.kr1 = n_kr;
+        }
+        it.t = t;
         int i = 0;
         while (i + 1 < E && u(s_first[i + 1]) <= t) ++i;
         const int rem = t - u(s_first[i]);
@@ -391,19 +424,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // (h = 0..3) for tokens 16 jfrag .. + 16: lane l has weight rows
         // 4 (l / 16) .. + 4 of a group, for token l % 16.  GEMM1: groups
         // par, par + 2 are W1 rows, par + 4, par + 6 the same W3 rows.  A
-        // K chunk of a tile (kc > 1) leaves its raw fp32 sums in its slice
-        // of `part` for stream_reduce_kernel (GEMM1: u at column n, v at
-        // column N + n of a 2N-wide row).
+        // piece of a split tile leaves its raw fp32 sums in its slice of
+        // `part` for stream_reduce_kernel (GEMM1: u at column n, v at
+        // column N + n of a 2N-wide row); the first piece also records the
+        // tile's piece count for each of its rows.
         const int m = 16 * jfrag + lr;
         if (m < cti.mrem) {
             const int64_t row = cti.row0 + m;
+            // piece of this item in its tile (K order) and the tile's pieces
+            const int first = split ? wg_of(cit.t * n_kr) : (int)blockIdx.x;
+            const int piece = (int)blockIdx.x - first;
+            if (split && piece == 0 && par == 0 && lq == 0)
+                np_of[row * col_tiles + cti.n0 / kCols] = wg_of(cit.t * n_kr + n_kr - 1) - first + 1;
 #pragma unroll
             for (int h = 0; h < (SWIGLU ? 2 : 4); ++h) {
                 const int n = cti.n0 + 16 * (par + 2 * h) + 4 * lq;
                 if (n < N) {
-                    if (kc > 1) {
+                    if (split) {
                         constexpr int W = SWIGLU ? 2 : 1;
-                        float *sl = slices + ((int64_t)cit.chunk * A + row) * (W * N);
+                        float *sl = slices + ((int64_t)piece * A + row) * (W * N);
                         *(f32x4 *)(sl + n) = acc[h];
                         if constexpr (SWIGLU) *(f32x4 *)(sl + N + n) = acc[h + 2];
                     } else {
@@ -435,7 +474,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     wait_vmcnt_lgkm0<0>();  // the trailing reloads land before the wave ends
 
-    // The decode layer's combine (GEMM2, fp32 outputs, one K chunk): this
+    // The decode layer's combine (GEMM2, fp32 outputs, whole tiles): this
     // workgroup's tiles are counted in their column blocks; the workgroup
     // that completes a block (every token tile of every expert on its
     // columns stored) forms y on those columns for all T tokens.  The
@@ -444,7 +483,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // them with agent-coherent loads: no cache flush or invalidation (those
     // stall the other workgroups of the XCD still streaming).
     if constexpr (!SWIGLU && std::is_same<TO, float>::value) {
-        if (fz.y && kc == 1) {
+        if (fz.y && !split) {
             __shared__ int s_done;
             __syncthreads();
             const int per_block = tiles / col_tiles;  // token tiles of all experts
@@ -499,32 +538,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-// The K chunks' partial sums added in chunk order (so the sum is the same
-// on every run), then the epilogue: GEMM2 out[r][n] = sum_c o_c[r][n];
-// GEMM1 out[r][n] = silu(sum_c u_c[r][n]) * sum_c v_c[r][n].  Nothing to do
-// when the GEMM kernel chose one chunk.  Only the rows the experts own,
+// The pieces of split tiles added in K order (so the sum is the same on
+// every run), then the epilogue: GEMM2 out[r][n] = sum_p o_p[r][n]; GEMM1
+// out[r][n] = silu(sum_p u_p[r][n]) * sum_p v_p[r][n].  Nothing to do when
+// the GEMM kernel kept whole tiles.  Only the rows the experts own,
 // [offsets[0], offsets[E]) clamped to [0, A) as the tile table clamps them,
 // are written: rows outside belong to no tile, their slices hold nothing.
 template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restrict__ part,
                                                             const int32_t *__restrict__ offsets,
-                                                            int E, int64_t A, int N,
+                                                            int E, int64_t A, int N, int kc_max,
                                                             TO *__restrict__ out) {
-    const int kc = *(const int *)part;
-    if (kc <= 1) return;
+    if (*(const int *)part <= 1) return;
     const float *slices = part + kSPartHdr;
     constexpr int W = SWIGLU ? 2 : 1;
+    constexpr int kCols = SWIGLU ? kSRowsT / 2 : kSRowsT;  // output columns per tile
+    const int col_tiles = (N + kCols - 1) / kCols;
+    const int64_t slice = A * (int64_t)(W * N);  // floats per piece
+    const int32_t *np_of = (const int32_t *)(slices + kc_max * slice);
     const int64_t lo = min<int64_t>(max(offsets[0], 0), A);
     const int64_t hi = min<int64_t>(max<int64_t>(offsets[E], lo), A);
-    const int64_t n4 = hi * N / 4;              // N is a multiple of 512
-    const int64_t slice = A * (int64_t)(W * N);  // floats per chunk
+    const int64_t n4 = hi * N / 4;  // N is a multiple of 512
     for (int64_t i = lo * N / 4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
          i += (int64_t)gridDim.x * 256) {
         const int64_t r = (4 * i) / N, n = (4 * i) % N;
+        const int np = min(max(np_of[r * col_tiles + n / kCols], 1), kc_max);
         const float *p = slices + r * (W * N) + n;
         f32x4 uu = *(const f32x4 *)p, vv = {};
         if constexpr (SWIGLU) vv = *(const f32x4 *)(p + N);
-        for (int c = 1; c < kc; ++c) {
+        for (int c = 1; c < np; ++c) {
             uu += *(const f32x4 *)(p + c * slice);
             if constexpr (SWIGLU) vv += *(const f32x4 *)(p + c * slice + N);
         }
@@ -535,18 +577,77 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restr
     }
 }
 
+// GEMM2 of the decode layer at the smallest batches: its expert outputs
+// (the pieces' sums as stream_reduce_kernel forms them, or `o` itself when
+// the GEMM kept whole tiles) go straight into the combine, y[t] =
+// residual[t] + sum_j g_j o[row_of[t][j]] with one fused multiply-add per
+// slot in slot order, as combine_kernel forms it, rounded once to bf16.
+__global__ __launch_bounds__(256) void stream_reduce_combine_kernel(
+    const float *__restrict__ part, const float *__restrict__ o,
+    const int32_t *__restrict__ row_of, const float *__restrict__ gw,
+    const bf16_t *__restrict__ residual, int64_t T, int k, int64_t A, int N, int kc_max,
+    bf16_t *__restrict__ y) {
+    const bool split = *(const int *)part > 1;
+    const float *slices = part + kSPartHdr;
+    const int col_tiles = (N + kSRowsT - 1) / kSRowsT;
+    const int64_t slice = A * (int64_t)N;
+    const int32_t *np_of = (const int32_t *)(slices + kc_max * slice);
+    const int n8 = N / 8;  // N is a multiple of 512
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * n8;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t t = i / n8;
+        const int n = (int)(i - t * n8) * 8;
+        float acc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int r = row_of[t * k + j];
+            if (r < 0) continue;
+            const float g = gw[t * k + j];
+            const float *p = (split ? slices : o) + (int64_t)r * N + n;
+            f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+            if (split) {
+                const int np = min(max(np_of[(int64_t)r * col_tiles + n / kSRowsT], 1), kc_max);
+                for (int c = 1; c < np; ++c) {
+                    a += *(const f32x4 *)(p + c * slice);
+                    b += *(const f32x4 *)(p + c * slice + 4);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[c] = fmaf(g, a[c], acc[c]);
+                acc[4 + c] = fmaf(g, b[c], acc[4 + c]);
+            }
+        }
+        if (residual) {
+            const uint4 rv = *(const uint4 *)(residual + t * N + n);
+            const uint32_t w4[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += bf16_bits_to_f32(w4[q] & 0xffffu);
+                acc[2 * q + 1] += bf16_bits_to_f32(w4[q] >> 16);
+            }
+        }
+        *(uint4 *)(y + t * N + n) =
+            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    }
+}
+
 namespace {
 
-// Most K chunks a launch may cut its tiles into: only at the smallest
-// batches (fewer than four rows per expert on average), where the tile count
-// can leave CUs idle.  The kernel picks the count it uses.
-int stream_chunk_limit(int64_t A, int E) { return (A > 0 && A < 4 * (int64_t)E) ? 4 : 1; }
+// Most pieces a tile may be split into: only at the smallest batches (fewer
+// than four rows per expert on average), where the tile count can leave CUs
+// idle.  The kernel decides whether to split.
+int stream_chunk_limit(int64_t A, int E) { return (A > 0 && A < 4 * (int64_t)E) ? 8 : 1; }
 
+// `reduce`: also launch the pass that sums split tiles' pieces (the decode
+// layer's GEMM2 leaves that to stream_reduce_combine_kernel).
 template <bool SWIGLU, typename TO>
 hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
                          void *out, int kc_max, float *part, hipStream_t s,
-                         const StreamFuse &fz = StreamFuse{}) {
+                         const StreamFuse &fz = StreamFuse{}, bool reduce = true) {
     hipError_t err = set_lds_limit<stream_gemm_kernel<SWIGLU, TO>>(kSLds);
     if (err != hipSuccess) return err;
     // one workgroup per CU, never more than there can be items:
@@ -557,11 +658,11 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather,
     hipLaunchKernelGGL((stream_gemm_kernel<SWIGLU, TO>), dim3(grid), dim3(256), kSLds, s,
                        (const bf16_t *)act, act_ld, gather, (const bf16_t *)Wa,
                        (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, kc_max, part, fz);
-    if ((err = hipGetLastError()) != hipSuccess || kc_max == 1) return err;
+    if ((err = hipGetLastError()) != hipSuccess || kc_max == 1 || !reduce) return err;
     const int64_t n4 = A * N / 4;  // N is a multiple of 512
     const int rgrid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
     hipLaunchKernelGGL((stream_reduce_kernel<SWIGLU, TO>), dim3(rgrid), dim3(256), 0, s,
-                       (const float *)part, offsets, E, A, N, (TO *)out);
+                       (const float *)part, offsets, E, A, N, kc_max, (TO *)out);
     return hipGetLastError();
 }
 
@@ -569,10 +670,14 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather,
 
 size_t stream_partial_bytes(int64_t A, int d, int d_ff, int E) {
     // header + the larger of GEMM1's (u and v: 2 d_ff per row) and GEMM2's
-    // (d per row) chunk slices; the two launches run one after the other
+    // (d per row) piece slices + the piece counts per row and column tile;
+    // the two launches run one after the other
     const int kc = stream_chunk_limit(A, E);
     if (kc == 1) return 0;
-    return sizeof(float) * ((size_t)kSPartHdr + (size_t)kc * A * std::max(2 * d_ff, d));
+    const size_t col_tiles = std::max((d_ff + kSRowsT / 2 - 1) / (kSRowsT / 2),
+                                      (d + kSRowsT - 1) / kSRowsT);
+    return sizeof(float) * ((size_t)kSPartHdr + (size_t)kc * A * std::max(2 * d_ff, d)) +
+           sizeof(int32_t) * (size_t)A * col_tiles;
 }
 
 bool stream_supported(int64_t A, int d, int d_ff, int E) {
@@ -580,8 +685,6 @@ bool stream_supported(int64_t A, int d, int d_ff, int E) {
     return d % kSKRange == 0 && d_ff % kSKRange == 0 && d >= kSKRange && d_ff >= kSKRange &&
            A <= kSMapMax && E <= 64;
 }
-
-bool stream_combines(int64_t A, int E) { return stream_chunk_limit(A, E) == 1; }
 
 int stream_combine_counters(int d) { return (d + kSRowsT - 1) / kSRowsT; }
 
@@ -591,8 +694,9 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
                                hipEvent_t gemm1_done, hipStream_t s) {
     int kc = stream_chunk_limit(A, E);
     if (kc > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) kc = 1;
-    // GEMM1 reads token rows through the map it builds; GEMM2's combine only
-    // runs where its tiles hold whole K (one chunk)
+    // GEMM1 reads token rows through the map it builds.  GEMM2 combines in
+    // its own tail where its tiles are never split (kc == 1); else the pass
+    // that sums its pieces forms y.
     StreamFuse f1 = fuse;
     f1.ctr_n = fuse.y && kc == 1 ? stream_combine_counters(d) : 0;
     f1.gw = nullptr;
@@ -607,8 +711,15 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
         f2 = fuse;
         f2.topk_idx = nullptr;
     }
-    return launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, fuse.offsets, E, d, d_ff,
-                                       A, out, kc, partial, s, f2);
+    err = launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, fuse.offsets, E, d, d_ff,
+                                      A, out, kc, partial, s, f2, !(kc > 1 && fuse.y));
+    if (err != hipSuccess || kc == 1 || !fuse.y) return err;
+    const int64_t T = fuse.T, n8 = T * d / 8;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n8 + 255) / 256));
+    hipLaunchKernelGGL(stream_reduce_combine_kernel, dim3(grid), dim3(256), 0, s,
+                       (const float *)partial, (const float *)out, fuse.row_of, fuse.gw,
+                       fuse.residual, T, fuse.k, A, d, kc, fuse.y);
+    return hipGetLastError();
 }
 
 hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,

@@ -291,9 +291,9 @@ def test_pieces_expert_ffn_and_combine():
 def test_expert_ffn_leaves_rows_past_the_experts_untouched():
     """moe_expert_ffn writes exactly the rows the experts own.  At the
     smallest batches (fewer than four rows per expert) the weight-streaming
-    kernels cut every tile's K ranges into chunks and sum them in a second
-    pass; with offsets[E] below T*k the rows past it belong to no expert and
-    must keep their contents bit for bit."""
+    kernels split tiles along K into pieces and sum them in a second pass;
+    with offsets[E] below T*k the rows past it belong to no expert and must
+    keep their contents bit for bit."""
     T, k, E, d, d_ff = 12, 2, 8, 2048, 2048
     w = Workload("ffn-rows", 41, T=T, d=d, d_ff=d_ff, E=E, k=k)
     assert moe.moe_expert_ffn_kernels(T, d, d_ff, E, k, torch.bfloat16) == "stream_gemm_kernel"
