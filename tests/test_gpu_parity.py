@@ -72,6 +72,13 @@ SMALL = [
     # taking all eight experts
     Workload("e1-k1", 27, T=50, d=256, d_ff=512, E=1, k=1),
     Workload("k-all", 28, T=40, d=256, d_ff=256, E=8, k=8),
+    # the weight stream's even K split with few tiles: GEMM1 8 tiles of
+    # 8 K ranges on 64 workgroups (8 pieces a tile) ...
+    Workload("split-8-pieces", 29, T=1, d=4096, d_ff=512, E=4, k=1),
+    # ... GEMM2 8 tiles of 14 K ranges on 56 workgroups (7 pieces a tile)
+    Workload("split-7-pieces", 30, T=1, d=512, d_ff=7168, E=8, k=2),
+    # ... both GEMMs split, pieces of 1-3 ranges crossing tile boundaries
+    Workload("split-3-tokens", 31, T=3, d=1024, d_ff=3584, E=8, k=2),
 ]
 
 
