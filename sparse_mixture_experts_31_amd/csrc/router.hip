@@ -232,22 +232,23 @@ constexpr int kRouterLdsBytes = 128 * 1024;  // most Wg bytes held in LDS
 // Many tokens: every wave of router_topk_kernel's one-wave-per-token form
 // reads all of Wg (E d fp32) per token, which at thousands of tokens makes
 // the router an L2 stream of T times Wg.  Here a workgroup copies Wg into
-// LDS once and its eight waves walk tokens (wave w of workgroup b: tokens
-// 8 b + w, then a grid further).  A lane covers the same elements of d in
-// the same order with the same fp64 steps and the same wave reduction as the
-// one-wave-per-token form of router_topk_kernel (WPT = 1, which the load
-// statistics use from 1024 tokens on), so those two give the same scores bit
-// for bit.  Below 1024 tokens both entry points use the four-wave form
-// (WPT = 4), whose fp64 partial sums meet in a different order: a score may
-// then differ from the one-wave form's in its last fp32 bit, rarely.  The
-// token's row is fetched eight pieces at a time so its loads are in flight
-// together.
-template <typename Tin, int Q>
+// LDS once and its eight waves walk groups of TPW consecutive tokens (wave w
+// of workgroup b: group 8 b + w, then a grid further).  For each token a
+// lane covers the same elements of d in the same order with the same fp64
+// steps and the same wave reduction as the one-wave-per-token form of
+// router_topk_kernel (WPT = 1, which the load statistics use from 1024
+// tokens on), so those two give the same scores bit for bit.  Below 1024
+// tokens both entry points use the four-wave form (WPT = 4), whose fp64
+// partial sums meet in a different order: a score may then differ from the
+// one-wave form's in its last fp32 bit, rarely.  A group's tokens share
+// each Wg value read from LDS and its conversion to fp64, and the next
+// 512-element piece of their rows is loaded while the current one is used.
+template <typename Tin, int TPW>
 __global__ __launch_bounds__(kRouterLdsWaves * kWave) void router_topk_lds_kernel(
     const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,
     int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits) {
     extern __shared__ __attribute__((aligned(16))) float s_wg[];  // [E][d]
-    __shared__ float s_logit[kRouterLdsWaves][64];
+    __shared__ float s_logit[kRouterLdsWaves][TPW][64];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     // Wg into LDS, sixteen 16-byte loads in flight per thread
@@ -265,45 +266,64 @@ __global__ __launch_bounds__(kRouterLdsWaves * kWave) void router_topk_lds_kerne
     __syncthreads();
 
     constexpr int kStep = kWave * 8;  // elements of d per lane step
-    for (int64_t t = (int64_t)blockIdx.x * kRouterLdsWaves + wave; t < T;
-         t += (int64_t)gridDim.x * kRouterLdsWaves) {
-        const Tin *xr = x + t * (int64_t)d;
+    const int npiece = d / kStep;     // d is a multiple of 512
+    for (int64_t t0 = ((int64_t)blockIdx.x * kRouterLdsWaves + wave) * TPW; t0 < T;
+         t0 += (int64_t)gridDim.x * kRouterLdsWaves * TPW) {
+        const Tin *xr[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)  // rows past T repeat the last row; never stored
+            xr[t] = x + min(t0 + t, T - 1) * (int64_t)d + lane * 8;
         for (int e0 = 0; e0 < E; e0 += 8) {
-            double acc[8];
+            double acc[TPW][8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-            // d is a multiple of Q kStep: Q pieces of the row per batch
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[t][j] = 0.0;
+            float xv[TPW][8], xn[TPW][8];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) load8<Tin>(xr[t], xv[t]);
 #pragma unroll 1
-            for (int i0 = lane * 8; i0 < d; i0 += Q * kStep) {
-                float xv[Q][8];
+            for (int p = 0; p < npiece; ++p) {
+                const int pn = min(p + 1, npiece - 1);  // the next piece (the last reloads itself)
 #pragma unroll
-                for (int q = 0; q < Q; ++q) load8<Tin>(xr + i0 + q * kStep, xv[q]);
+                for (int t = 0; t < TPW; ++t) load8<Tin>(xr[t] + pn * kStep, xn[t]);
+                // experts innermost: 8 TPW independent chains (experts past E
+                // read a valid row; their sums are never stored)
+                float wv[8][8];
 #pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    // experts innermost: eight independent chains (experts
-                    // past E read a valid row; their sums are never stored)
-                    float wv[8][8];
+                for (int j = 0; j < 8; ++j)
+                    load8<float>(s_wg + min(e0 + j, E - 1) * d + lane * 8 + p * kStep, wv[j]);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        load8<float>(s_wg + min(e0 + j, E - 1) * d + i0 + q * kStep, wv[j]);
+                for (int c = 0; c < 8; ++c) {
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
+                    for (int t = 0; t < TPW; ++t)
 #pragma unroll
                         for (int j = 0; j < 8; ++j)
-                            acc[j] = fma((double)xv[q][c], (double)wv[j][c], acc[j]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+                            acc[t][j] = fma((double)xv[t][c], (double)wv[j][c], acc[t][j]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) xv[t][c] = xn[t][c];
             }
-            wave_reduce_halving<8>(acc, lane);
-            if ((lane & 7) == 0 && e0 + lane / 8 < E) s_logit[wave][e0 + lane / 8] = (float)acc[0];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                wave_reduce_halving<8>(acc[t], lane);
+                if ((lane & 7) == 0 && e0 + lane / 8 < E)
+                    s_logit[wave][t][e0 + lane / 8] = (float)acc[t][0];
+            }
         }
-        if (out_logits && lane < E) out_logits[t * E + lane] = s_logit[wave][lane];
-        if (lane == 0) {
+        if (out_logits)
+            for (int q = lane; q < TPW * E; q += kWave) {
+                const int t = q / E, e = q % E;
+                if (t0 + t < T) out_logits[(t0 + t) * E + e] = s_logit[wave][t][e];
+            }
+        if (lane < TPW && t0 + lane < T) {
             int sel[8];
             float sl[8];
-            select_topk(s_logit[wave], E, k, sel, sl);
-            write_choice(t, k, sel, sl, out_idx, out_w);
+            select_topk(s_logit[wave][lane], E, k, sel, sl);
+            write_choice(t0 + lane, k, sel, sl, out_idx, out_w);
         }
     }
 }
@@ -365,30 +385,31 @@ namespace {
 // tokens: one wave per token, four tokens per workgroup, or the LDS kernel.
 bool router_wide_rows(int64_t T) { return T < 1024; }
 
-template <typename Tin, int Q>
-hipError_t launch_router_lds_q(const Tin *x, const float *Wg, int64_t T, int d, int E, int k,
+template <typename Tin, int TPW>
+hipError_t launch_router_lds_t(const Tin *x, const float *Wg, int64_t T, int d, int E, int k,
                                int32_t *idx, float *gw, float *logits, hipStream_t s) {
     using namespace moe;
     const int bytes = E * d * (int)sizeof(float);  // <= kRouterLdsBytes
-    hipError_t err = set_lds_limit<router_topk_lds_kernel<Tin, Q>>(kRouterLdsBytes);
+    hipError_t err = set_lds_limit<router_topk_lds_kernel<Tin, TPW>>(kRouterLdsBytes);
     if (err != hipSuccess) return err;
-    const int64_t blocks =
-        std::min<int64_t>(device_cus(), (T + kRouterLdsWaves - 1) / kRouterLdsWaves);
-    hipLaunchKernelGGL((router_topk_lds_kernel<Tin, Q>), dim3((unsigned)blocks),
+    const int64_t per_block = (int64_t)kRouterLdsWaves * TPW;
+    const int64_t blocks = std::min<int64_t>(device_cus(), (T + per_block - 1) / per_block);
+    hipLaunchKernelGGL((router_topk_lds_kernel<Tin, TPW>), dim3((unsigned)blocks),
                        dim3(kRouterLdsWaves * kWave), bytes, s, x, Wg, T, d, E, k, idx, gw,
                        logits);
     return hipGetLastError();
 }
 
-// Row pieces per batch: the most of 8, 4, 2, 1 that divides d / 512.
+// Tokens per wave: two once that still gives every CU a workgroup.  (On
+// MI355X two tokens per wave take the T = 4096 router from 32.3 to 30.8 us
+// and the T = 16384 one from 99 to 87 us; four were eight times slower.)
 template <typename Tin>
 hipError_t launch_router_lds(const Tin *x, const float *Wg, int64_t T, int d, int E, int k,
                              int32_t *idx, float *gw, float *logits, hipStream_t s) {
-    const int n = d / 512;
-    if (n % 8 == 0) return launch_router_lds_q<Tin, 8>(x, Wg, T, d, E, k, idx, gw, logits, s);
-    if (n % 4 == 0) return launch_router_lds_q<Tin, 4>(x, Wg, T, d, E, k, idx, gw, logits, s);
-    if (n % 2 == 0) return launch_router_lds_q<Tin, 2>(x, Wg, T, d, E, k, idx, gw, logits, s);
-    return launch_router_lds_q<Tin, 1>(x, Wg, T, d, E, k, idx, gw, logits, s);
+    const int64_t full = (int64_t)moe::kRouterLdsWaves * moe::device_cus();  // waves in one pass
+    if (T >= 2 * full)
+        return launch_router_lds_t<Tin, 2>(x, Wg, T, d, E, k, idx, gw, logits, s);
+    return launch_router_lds_t<Tin, 1>(x, Wg, T, d, E, k, idx, gw, logits, s);
 }
 
 template <bool STATS>
