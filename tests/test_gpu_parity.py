@@ -368,6 +368,32 @@ def test_runs_are_bit_identical():
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("name", ["stream-tiles", "split-3-tokens", "grouped-bf16",
+                                  "wide-narrow"])
+def test_side_streams_give_the_default_streams_result(name):
+    """moe_forward on two side streams at once, each with its own output and
+    workspace, matches the default stream's result bit for bit: every launch
+    of the layer goes to the stream it is given, and nothing is shared
+    between calls."""
+    w = next(v for v in SMALL if v.name == name)
+    L = _case(w)
+    y0 = moe.moe_forward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.k)
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    outs = []
+    for s in (torch.cuda.Stream(), torch.cuda.Stream()):   # default priority
+        s.wait_stream(cur)
+        with torch.cuda.stream(s):
+            y = torch.empty_like(L["x"])
+            ws = moe.workspace(w.T, w.d, w.d_ff, w.E, w.k, L["x"].dtype, L["x"].device)
+            moe.moe_forward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.k, y=y, ws=ws,
+                            stream=s)
+            outs.append(y)
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y, y0)
+
+
 def test_rmsnorm_matches_oracle_bit_for_bit():
     h = (torch.randn((333, 4096), device=DEV) * 3).to(torch.bfloat16)
     eps = float(np.float32(1e-5))
@@ -566,7 +592,7 @@ def decode16():
     return w, _case(w)
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 12, 15, 16])
 def test_decode_sweep(decode16, T):
     """Mixtral-shaped decode batches of 1..16 tokens: each token takes exactly
     two experts, so T tokens touch at most min(8, 2T) of them (expected
