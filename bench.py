@@ -46,6 +46,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self) -> int:
         e = ctypes.c_void_p()
@@ -64,6 +65,12 @@ class HipEvents:
 
     def destroy(self, e: int):
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+    def record(self, e: int, stream):
+        """Record e on a torch stream (the stream the timed work runs on)."""
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
 
 def gemm1_work(w, counts):
@@ -299,6 +306,48 @@ def time_layer(w, L, moe, np, torch, ev, stream, steps, warmup, blocks=None):
     return ms_per_step, gemm1_ms, breakdown
 
 
+def ep_shard(Ms, steps, warmup, dev, seed, moe, np, torch, ev, stream):
+    """One GPU's share under expert parallelism (one expert per GPU): the
+    expert GEMMs of a single Mixtral-sized expert (E = 1) on M received rows,
+    timed with HIP events around every call of moe_expert_ffn."""
+    from sparse_mixture_experts_31_amd.inputs import Workload, make_layer
+    res = {}
+    for M in Ms:
+        w = Workload("ep-shard", 5, T=M, d=4096, d_ff=14336, E=1, k=1)
+        L = make_layer(w, dev, seed)
+        offsets = torch.tensor([0, M], dtype=torch.int32, device=dev)
+        ws = moe.workspace(M, w.d, w.d_ff, 1, 1, L["x"].dtype, dev)
+        out = torch.empty_like(L["x"])
+
+        def call():
+            moe.moe_expert_ffn(L["x"], offsets, L["W1"], L["W3"], L["W2"], M, 1, out_perm=out,
+                               ws=ws, stream=stream)
+
+        for _ in range(warmup):
+            call()
+        pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+        for a, b in pairs:
+            ev.record(a, stream)
+            call()
+            ev.record(b, stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+        for a, b in pairs:
+            ev.destroy(a)
+            ev.destroy(b)
+        flops = 2.0 * M * 3 * w.d * w.d_ff
+        nbytes = 3.0 * w.d * w.d_ff * 2 + 2.0 * M * w.d * 2
+        res[str(M)] = {"kernel": moe.moe_expert_ffn_kernels(M, w.d, w.d_ff, 1, 1, w.torch_dtype),
+                       "ms": round(ms, 4),
+                       "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                       "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del L, ws, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +366,9 @@ def main():
                     help="skip the prefill (T = 4096) layer the decode run also times")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="oracle sample size (default sized to ~10-30 s)")
+    ap.add_argument("--ep-shard", default=None, metavar="M1,M2,...",
+                    help="only time one GPU's share under expert parallelism: the expert "
+                         "GEMMs of one Mixtral-sized expert on M rows, for each M, and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (a plain copy of known "
                          "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -345,6 +397,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.ep_shard:
+        ev = HipEvents()
+        Ms = [int(m) for m in args.ep_shard.split(",")]
+        res = ep_shard(Ms, args.steps, min(args.warmup, 20), dev, args.seed, moe, np, torch, ev,
+                       torch.cuda.current_stream())
+        print(json.dumps({"ep_shard": res, "d": 4096, "d_ff": 14336, "dtype": "bf16",
+                          "steps": args.steps, "data": "synthetic"}), flush=True)
         return
     w = WORKLOADS[args.workload]
     print(f"[bench] workload {w.name}: T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} k={w.k} "

@@ -51,7 +51,8 @@ constexpr int kSWStage = kSGrp * 1024;
 constexpr int kSTokBuf = kSBT * 1024;
 constexpr int kSMapMax = 33 * 64;  // token_of entries: A < 33 E on this path, E <= 64
 constexpr int kSLds = kSP * kSWStage + 2 * kSTokBuf + kSMapMax * 4;
-constexpr int kSPartHdr = 64;  // floats before the chunk slices (the chosen chunk count)
+constexpr int kSPartHdr = 64;  // header ints of `part`: [0] split taken, [1] the grid
+constexpr int kSSlot = kSBT * kSRowsT;  // floats in a slot: one tile's 32 x 128 fp32 sums
 static_assert(kSLds <= 160 * 1024 - 3 * 1024, "LDS capacity (3 KiB of static tables)");
 static_assert(kSGrp == 16 && kSGroups == 8, "one 16-row MFMA fragment per stage, 8 per K range");
 static_assert(kSP - 1 <= kSGroups / 2, "prologue stages carry no token loads");
@@ -193,8 +194,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // Work split.  Whole tiles, workgroup b taking the run of tiles
     // [b tiles / NG, (b + 1) tiles / NG) (a run of neighbouring column tiles
     // of one expert streams 3 % faster on MI355X than tiles dealt round
-    // robin); or, allowed at the smallest batches (kc_max > 1) where a few
-    // tiles leave CUs idle for much of the kernel, an even split of all
+    // robin); or, where the launcher allows it (kc_max > 1: scratch for the
+    // partial sums is there) and whole tiles would leave CUs idle for much of
+    // the kernel (few tiles, or a last round mostly empty), an even split of all
     // R = tiles x n_kr K ranges in tile order: workgroup b of the NGe used
     // walks ranges [b R / NGe, (b + 1) R / NGe), cut at tile boundaries into
     // items.  A tile's pieces (at most kc_max: NGe is kept small enough that
@@ -216,11 +218,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         split = 10 * ((R + NGe - 1) / NGe) <= 9 * whole;
         if (!split) NGe = NG;
     }
-    if (kc_max > 1 && blockIdx.x == 0 && tid == 0) *(int *)part = split ? kc_max : 1;
-    float *const slices = part + kSPartHdr;
-    // pieces of the tile holding (row r, column tile c) at [r * col_tiles + c]
-    int32_t *const np_of =
-        split ? (int32_t *)(slices + (int64_t)kc_max * A * ((SWIGLU ? 2 : 1) * N)) : nullptr;
+    if (kc_max > 1 && blockIdx.x == 0 && tid == 0) {
+        ((int *)part)[0] = split ? 1 : 0;
+        ((int *)part)[1] = NG;
+    }
+    // A piece of a split tile is always the first or the last item of its
+    // workgroup (the items between are whole tiles), so the pieces go to two
+    // slots per workgroup: slot 2 b for its first item, 2 b + 1 for its last.
+    // info[r * col_tiles + c] describes the tile holding row r and column
+    // tile c: r's row in the tile (bits 0-4), the tile's pieces (bits 5-8)
+    // and the slot of its first piece (from bit 9); the next pieces are in
+    // the first slots of the next workgroups.
+    float *const slots = part + kSPartHdr;
+    int32_t *const info = split ? (int32_t *)(slots + (int64_t)2 * NG * kSSlot) : nullptr;
     // (R < 2^31: tiles <= 33 x 224 x 64 experts, n_kr <= K / 512)
     const int g0 = split ? (int)((int64_t)blockIdx.x * R / NGe) : 0;
     const int g1 = split ? (int)(((int64_t)blockIdx.x + 1) * R / NGe) : 0;
@@ -424,27 +434,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // (h = 0..3) for tokens 16 jfrag .. + 16: lane l has weight rows
         // 4 (l / 16) .. + 4 of a group, for token l % 16.  GEMM1: groups
         // par, par + 2 are W1 rows, par + 4, par + 6 the same W3 rows.  A
-        // piece of a split tile leaves its raw fp32 sums in its slice of
-        // `part` for stream_reduce_kernel (GEMM1: u at column n, v at
-        // column N + n of a 2N-wide row); the first piece also records the
-        // tile's piece count for each of its rows.
+        // piece of a split tile leaves its raw fp32 sums in its slot for
+        // stream_reduce_kernel (GEMM1: u at column c of the tile, v at
+        // 64 + c); the workgroup of a tile's first piece describes the tile
+        // in `info` for each of its rows.
         const int m = 16 * jfrag + lr;
         if (m < cti.mrem) {
             const int64_t row = cti.row0 + m;
-            // piece of this item in its tile (K order) and the tile's pieces
-            const int first = split ? wg_of(cit.t * n_kr) : (int)blockIdx.x;
-            const int piece = (int)blockIdx.x - first;
-            if (split && piece == 0 && par == 0 && lq == 0)
-                np_of[row * col_tiles + cti.n0 / kCols] = wg_of(cit.t * n_kr + n_kr - 1) - first + 1;
+            int first = (int)blockIdx.x, np = 1;  // the tile's first workgroup and pieces
+            if (split) {
+                first = wg_of(cit.t * n_kr);
+                np = wg_of(cit.t * n_kr + n_kr - 1) - first + 1;
+            }
+            const int slot = 2 * (int)blockIdx.x + (ck == 0 ? 0 : 1);
+            if (split && first == (int)blockIdx.x && par == 0 && lq == 0)
+                info[row * col_tiles + cti.n0 / kCols] = m | (np << 5) | (slot << 9);
 #pragma unroll
             for (int h = 0; h < (SWIGLU ? 2 : 4); ++h) {
-                const int n = cti.n0 + 16 * (par + 2 * h) + 4 * lq;
+                const int c = 16 * (par + 2 * h) + 4 * lq;  // column in the tile
+                const int n = cti.n0 + c;
                 if (n < N) {
-                    if (split) {
-                        constexpr int W = SWIGLU ? 2 : 1;
-                        float *sl = slices + ((int64_t)piece * A + row) * (W * N);
-                        *(f32x4 *)(sl + n) = acc[h];
-                        if constexpr (SWIGLU) *(f32x4 *)(sl + N + n) = acc[h + 2];
+                    if (np > 1) {
+                        float *sl = slots + (int64_t)slot * kSSlot + m * kSRowsT + c;
+                        *(f32x4 *)sl = acc[h];
+                        if constexpr (SWIGLU) *(f32x4 *)(sl + kSRowsT / 2) = acc[h + 2];
                     } else {
                         float r[4];
 #pragma unroll
@@ -541,34 +554,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // The pieces of split tiles added in K order (so the sum is the same on
 // every run), then the epilogue: GEMM2 out[r][n] = sum_p o_p[r][n]; GEMM1
 // out[r][n] = silu(sum_p u_p[r][n]) * sum_p v_p[r][n].  Nothing to do when
-// the GEMM kernel kept whole tiles.  Only the rows the experts own,
+// the GEMM kernel kept whole tiles, or for the rows of tiles it did not
+// split (it stored those itself).  Only the rows the experts own,
 // [offsets[0], offsets[E]) clamped to [0, A) as the tile table clamps them,
-// are written: rows outside belong to no tile, their slices hold nothing.
+// are looked at: rows outside belong to no tile.
 template <bool SWIGLU, typename TO>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restrict__ part,
                                                             const int32_t *__restrict__ offsets,
-                                                            int E, int64_t A, int N, int kc_max,
+                                                            int E, int64_t A, int N,
                                                             TO *__restrict__ out) {
-    if (*(const int *)part <= 1) return;
-    const float *slices = part + kSPartHdr;
-    constexpr int W = SWIGLU ? 2 : 1;
+    const int *hdr = (const int *)part;
+    if (hdr[0] == 0) return;
+    const float *slots = part + kSPartHdr;
     constexpr int kCols = SWIGLU ? kSRowsT / 2 : kSRowsT;  // output columns per tile
     const int col_tiles = (N + kCols - 1) / kCols;
-    const int64_t slice = A * (int64_t)(W * N);  // floats per piece
-    const int32_t *np_of = (const int32_t *)(slices + kc_max * slice);
+    const int32_t *info = (const int32_t *)(slots + (int64_t)2 * hdr[1] * kSSlot);
     const int64_t lo = min<int64_t>(max(offsets[0], 0), A);
     const int64_t hi = min<int64_t>(max<int64_t>(offsets[E], lo), A);
     const int64_t n4 = hi * N / 4;  // N is a multiple of 512
     for (int64_t i = lo * N / 4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
          i += (int64_t)gridDim.x * 256) {
         const int64_t r = (4 * i) / N, n = (4 * i) % N;
-        const int np = min(max(np_of[r * col_tiles + n / kCols], 1), kc_max);
-        const float *p = slices + r * (W * N) + n;
+        const int v = info[r * col_tiles + n / kCols];
+        const int np = (v >> 5) & 15;
+        if (np <= 1) continue;  // a whole tile: stored by the GEMM kernel
+        const int m = v & 31, s0 = v >> 9, c = (int)(n % kCols);
+        const float *p = slots + (int64_t)s0 * kSSlot + m * kSRowsT + c;
         f32x4 uu = *(const f32x4 *)p, vv = {};
-        if constexpr (SWIGLU) vv = *(const f32x4 *)(p + N);
-        for (int c = 1; c < np; ++c) {
-            uu += *(const f32x4 *)(p + c * slice);
-            if constexpr (SWIGLU) vv += *(const f32x4 *)(p + c * slice + N);
+        if constexpr (SWIGLU) vv = *(const f32x4 *)(p + kSRowsT / 2);
+        for (int q = 1; q < np; ++q) {
+            // piece q: the first slot of workgroup s0 / 2 + q
+            const float *pq = slots + (int64_t)(2 * (s0 / 2 + q)) * kSSlot + m * kSRowsT + c;
+            uu += *(const f32x4 *)pq;
+            if constexpr (SWIGLU) vv += *(const f32x4 *)(pq + kSRowsT / 2);
         }
         float o[4];
 #pragma unroll
@@ -577,21 +595,20 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restr
     }
 }
 
-// GEMM2 of the decode layer at the smallest batches: its expert outputs
-// (the pieces' sums as stream_reduce_kernel forms them, or `o` itself when
-// the GEMM kept whole tiles) go straight into the combine, y[t] =
+// GEMM2 of the decode layer where its tiles may be split: its expert
+// outputs (the pieces' sums as stream_reduce_kernel forms them for split
+// tiles, `o` itself for the others) go straight into the combine, y[t] =
 // residual[t] + sum_j g_j o[row_of[t][j]] with one fused multiply-add per
 // slot in slot order, as combine_kernel forms it, rounded once to bf16.
 __global__ __launch_bounds__(256) void stream_reduce_combine_kernel(
     const float *__restrict__ part, const float *__restrict__ o,
     const int32_t *__restrict__ row_of, const float *__restrict__ gw,
-    const bf16_t *__restrict__ residual, int64_t T, int k, int64_t A, int N, int kc_max,
-    bf16_t *__restrict__ y) {
-    const bool split = *(const int *)part > 1;
-    const float *slices = part + kSPartHdr;
+    const bf16_t *__restrict__ residual, int64_t T, int k, int N, bf16_t *__restrict__ y) {
+    const int *hdr = (const int *)part;
+    const bool split = hdr[0] != 0;
+    const float *slots = part + kSPartHdr;
     const int col_tiles = (N + kSRowsT - 1) / kSRowsT;
-    const int64_t slice = A * (int64_t)N;
-    const int32_t *np_of = (const int32_t *)(slices + kc_max * slice);
+    const int32_t *info = (const int32_t *)(slots + (int64_t)2 * hdr[1] * kSSlot);
     const int n8 = N / 8;  // N is a multiple of 512
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * n8;
          i += (int64_t)gridDim.x * 256) {
@@ -604,13 +621,23 @@ __global__ __launch_bounds__(256) void stream_reduce_combine_kernel(
             const int r = row_of[t * k + j];
             if (r < 0) continue;
             const float g = gw[t * k + j];
-            const float *p = (split ? slices : o) + (int64_t)r * N + n;
-            f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
-            if (split) {
-                const int np = min(max(np_of[(int64_t)r * col_tiles + n / kSRowsT], 1), kc_max);
-                for (int c = 1; c < np; ++c) {
-                    a += *(const f32x4 *)(p + c * slice);
-                    b += *(const f32x4 *)(p + c * slice + 4);
+            const int v = split ? info[(int64_t)r * col_tiles + n / kSRowsT] : 0;
+            const int np = (v >> 5) & 15;
+            f32x4 a, b;
+            if (np <= 1) {
+                const float *p = o + (int64_t)r * N + n;
+                a = *(const f32x4 *)p;
+                b = *(const f32x4 *)(p + 4);
+            } else {
+                const int m = v & 31, s0 = v >> 9, c0 = n % kSRowsT;
+                const float *p = slots + (int64_t)s0 * kSSlot + m * kSRowsT + c0;
+                a = *(const f32x4 *)p;
+                b = *(const f32x4 *)(p + 4);
+                for (int q = 1; q < np; ++q) {
+                    const float *pq =
+                        slots + (int64_t)(2 * (s0 / 2 + q)) * kSSlot + m * kSRowsT + c0;
+                    a += *(const f32x4 *)pq;
+                    b += *(const f32x4 *)(pq + 4);
                 }
             }
 #pragma unroll
@@ -636,10 +663,19 @@ __global__ __launch_bounds__(256) void stream_reduce_combine_kernel(
 
 namespace {
 
-// Most pieces a tile may be split into: only at the smallest batches (fewer
-// than four rows per expert on average), where the tile count can leave CUs
-// idle.  The kernel decides whether to split.
-int stream_chunk_limit(int64_t A, int E) { return (A > 0 && A < 4 * (int64_t)E) ? 8 : 1; }
+// Most pieces a tile may be split into (the kernel decides whether to split).
+constexpr int kSMaxPieces = 8;
+
+// In the decode layer: may the tiles be split?  At the smallest batches
+// (fewer than four rows per expert on average), and wherever GEMM2 cannot
+// have tiles for half the CUs (one or a few experts), since there whole
+// tiles leave CUs idle.  Elsewhere GEMM2 keeps whole tiles and forms y in
+// its own tail.
+int stream_layer_pieces(int64_t A, int d, int E) {
+    if (A <= 0) return 1;
+    const int64_t max_tiles2 = ((A + kSBT - 1) / kSBT + E - 1) * ((d + kSRowsT - 1) / kSRowsT);
+    return (A < 4 * (int64_t)E || 2 * max_tiles2 <= device_cus()) ? kSMaxPieces : 1;
+}
 
 // `reduce`: also launch the pass that sums split tiles' pieces (the decode
 // layer's GEMM2 leaves that to stream_reduce_combine_kernel).
@@ -662,22 +698,21 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather,
     const int64_t n4 = A * N / 4;  // N is a multiple of 512
     const int rgrid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
     hipLaunchKernelGGL((stream_reduce_kernel<SWIGLU, TO>), dim3(rgrid), dim3(256), 0, s,
-                       (const float *)part, offsets, E, A, N, kc_max, (TO *)out);
+                       (const float *)part, offsets, E, A, N, (TO *)out);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t stream_partial_bytes(int64_t A, int d, int d_ff, int E) {
-    // header + the larger of GEMM1's (u and v: 2 d_ff per row) and GEMM2's
-    // (d per row) piece slices + the piece counts per row and column tile;
-    // the two launches run one after the other
-    const int kc = stream_chunk_limit(A, E);
-    if (kc == 1) return 0;
+    // header + two slots per workgroup (at most one per CU) + the tile
+    // description per row and column tile (the larger of GEMM1's and
+    // GEMM2's); the two launches run one after the other
+    (void)E;
     const size_t col_tiles = std::max((d_ff + kSRowsT / 2 - 1) / (kSRowsT / 2),
                                       (d + kSRowsT - 1) / kSRowsT);
-    return sizeof(float) * ((size_t)kSPartHdr + (size_t)kc * A * std::max(2 * d_ff, d)) +
-           sizeof(int32_t) * (size_t)A * col_tiles;
+    return sizeof(float) * ((size_t)kSPartHdr + (size_t)2 * device_cus() * kSSlot) +
+           sizeof(int32_t) * (size_t)std::max<int64_t>(A, 0) * col_tiles;
 }
 
 bool stream_supported(int64_t A, int d, int d_ff, int E) {
@@ -692,7 +727,7 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
                                int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
                                float *partial, size_t partial_bytes, const StreamFuse &fuse,
                                hipEvent_t gemm1_done, hipStream_t s) {
-    int kc = stream_chunk_limit(A, E);
+    int kc = stream_layer_pieces(A, d, E);
     if (kc > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) kc = 1;
     // GEMM1 reads token rows through the map it builds.  GEMM2 combines in
     // its own tail where its tiles are never split (kc == 1); else the pass
@@ -718,7 +753,7 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n8 + 255) / 256));
     hipLaunchKernelGGL(stream_reduce_combine_kernel, dim3(grid), dim3(256), 0, s,
                        (const float *)partial, (const float *)out, fuse.row_of, fuse.gw,
-                       fuse.residual, T, fuse.k, A, d, kc, fuse.y);
+                       fuse.residual, T, fuse.k, d, fuse.y);
     return hipGetLastError();
 }
 
@@ -727,9 +762,9 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
                              int64_t A, int d, int d_ff, int E, void *hbuf, void *out,
                              float *partial, size_t partial_bytes, hipEvent_t mid,
                              hipStream_t s) {
-    // K chunks only when the scratch for their partial sums is there
-    int kc = stream_chunk_limit(A, E);
-    if (kc > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) kc = 1;
+    // split tiles only when the scratch for their partial sums is there
+    int kc = kSMaxPieces;
+    if (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E)) kc = 1;
     hipError_t err = launch_stream<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A,
                                                  hbuf, kc, partial, s);
     if (err == hipSuccess && mid) err = hipEventRecord(mid, s);

@@ -324,6 +324,27 @@ def test_expert_ffn_leaves_rows_past_the_experts_untouched():
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("M", [8, 1024])
+def test_expert_parallel_shard_at_the_mixtral_shape(M):
+    """One GPU's share under expert parallelism (one expert per GPU): the
+    expert GEMMs of one Mixtral-sized expert on the M rows it received (8 at
+    decode, 1024 at prefill), every row (M = 8) or 24 sampled rows against
+    the oracle's expert."""
+    w = Workload("ep-shard", 5, T=M, d=4096, d_ff=14336, E=1, k=1)
+    L = _case(w)
+    offsets = torch.tensor([0, M], dtype=torch.int32, device=DEV)
+    out = moe.moe_expert_ffn(L["x"], offsets, L["W1"], L["W3"], L["W2"], M, 1)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if M <= 24 else np.sort(np.random.default_rng(M).choice(M, 24,
+                                                                               replace=False))
+    xr = to_np(L["x"]).astype(np.float64)
+    want = np.stack([oracle.swiglu_expert(xr[r], L["W1"], L["W3"], L["W2"], 0) for r in rows])
+    err = normwise(to_np(out)[rows], want)
+    log(f"  ep shard M={M} ({moe.moe_expert_ffn_kernels(M, 4096, 14336, 1, 1, torch.bfloat16)}):"
+        f" normwise {err:.3e} over {len(rows)} rows")
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("w", [
     Workload("forced", 20, T=200, d=256, d_ff=512),
     # decode-sized (T*k/E <= 24): the weight-streaming kernels, here with
