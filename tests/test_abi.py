@@ -55,6 +55,39 @@ def test_workspace_size_rules():
         assert ws(*bad, moe.MOE_BF16) == 0, bad
 
 
+def test_permute_workspace_size_rules():
+    """One workgroup groups up to 4096 assignments (no workspace); above that
+    the chunk counts need E ints per chunk, at most 512 chunks; the layer's
+    workspace always holds them."""
+    pw = moe.moe_permute_workspace_size
+    assert pw(2048, 8, 2) == 0 and pw(4096, 8, 1) == 0 and pw(0, 8, 2) == 0
+    assert pw(2049, 8, 2) == 4 * 17 * 8               # 4098 assignments, 17 chunks of 256
+    assert pw(16384, 8, 2) == 4 * 128 * 8
+    assert pw(1 << 20, 8, 2) <= 4 * 512 * 8           # chunks grow instead of their count
+    for bad in [(-1, 8, 2), (8, 65, 2), (8, 8, 9), (8, 4, 5), (8, 8, 0), (1 << 30, 8, 2)]:
+        assert pw(*bad) == 0, bad
+    for T in (1, 100, 2049, 4096, 16384):
+        assert moe.moe_workspace_size(T, 4096, 14336, 8, 2, moe.MOE_BF16) >= pw(T, 8, 2)
+
+
+def test_kernel_family_labels_follow_rows_per_expert():
+    """The expert kernels are chosen by rows per expert (T k / E) on the host:
+    the weight stream below 25, the 128 x 64 grouped kernels below 49, the
+    wide kernels above (128-row token tiles up to 100, then 256), bf16 only
+    for the stream and wide kernels."""
+    f = lambda T, E=8, k=2, dt=moe.MOE_BF16: moe.moe_expert_ffn_kernels(T, 4096, 14336, E, k, dt)
+    assert f(1) == f(99) == "stream_gemm_kernel"
+    assert f(100).startswith("grouped_gemm_kernel (128 x 64")
+    assert f(195).startswith("grouped_gemm_kernel (128 x 64")
+    assert f(196) == "wide_gemm_kernel (128-row token tiles)"
+    assert f(400) == "wide_gemm_kernel (128-row token tiles)"
+    assert f(401) == f(4096) == "wide_gemm_kernel (256-row token tiles)"
+    assert f(8, E=1, k=1) == "stream_gemm_kernel"          # one expert per GPU, decode share
+    assert f(1024, E=1, k=1) == "wide_gemm_kernel (256-row token tiles)"
+    assert not f(4096, dt=moe.MOE_F32).startswith("wide")
+    assert f(8, E=65) == ""
+
+
 def _rc(name, *args):
     return getattr(moe.lib(), name)(*args)
 
