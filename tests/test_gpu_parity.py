@@ -79,6 +79,9 @@ SMALL = [
     Workload("split-7-pieces", 30, T=1, d=512, d_ff=7168, E=8, k=2),
     # ... both GEMMs split, pieces of 1-3 ranges crossing tile boundaries
     Workload("split-3-tokens", 31, T=3, d=1024, d_ff=3584, E=8, k=2),
+    # ... and in a layer of two experts with 24 rows each, where GEMM2 has 16
+    # tiles (whole tiles would leave most CUs idle)
+    Workload("split-two-experts", 32, T=24, d=1024, d_ff=2048, E=2, k=2),
 ]
 
 
@@ -719,7 +722,7 @@ def _random_workload(seed):
     return Workload(f"random-{seed}", 200 + seed, T=T, d=d, d_ff=d_ff, E=E, k=k, dtype=dt)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_shapes(seed):
     """moe_forward on seeded random shapes (every kernel family and their
     thresholds) against the oracle on up to 48 sampled tokens."""
