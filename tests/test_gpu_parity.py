@@ -664,6 +664,20 @@ def test_decode_sweep(decode16, T):
     assert (counts > 0).sum() <= min(w.E, 2 * T)
 
 
+def test_weight_stream_at_every_small_batch():
+    """Every batch of 1..48 tokens (2..96 assignments over 8 experts) on a
+    small shape the weight-streaming kernels take: the even K split, whole
+    tiles, and the rule between them meet every token count; each layer
+    against the oracle on all its tokens."""
+    w0 = Workload("stream-every-T", 33, T=48, d=512, d_ff=1536)
+    L0 = _case(w0)
+    for T in range(1, 49):
+        w = w0.with_(name=f"stream-T{T}", T=T)
+        assert moe.moe_expert_ffn_kernels(T, w.d, w.d_ff, w.E, w.k,
+                                          torch.bfloat16) == "stream_gemm_kernel"
+        _forward_and_check(w, dict(L0, x=L0["x"][:T].contiguous()))
+
+
 def test_decode_single_token_reads_only_its_two_experts(decode16):
     """T = 1: NaN in the six experts the token does not choose must leave y
     bit for bit unchanged (their weights are never read)."""
