@@ -350,7 +350,7 @@ moe_status moe_forward(const void *x, const float *Wg, const void *W1, const voi
 // ---- the layer without a caller workspace ---------------------------------
 //
 // The fused layer's scratch (routing, grouping, SwiGLU rows, expert outputs,
-// K-chunk partial sums) lives in one file-scope device array instead of a
+// split-tile partial sums) lives in one file-scope device array instead of a
 // caller workspace.  Each GPU holds its own copy from the first call on it
 // until the process ends.  The array's name is a host-side stand-in in host
 // code: its device address comes from hipGetSymbolAddress, once per device,

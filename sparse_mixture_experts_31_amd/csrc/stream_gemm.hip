@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ gather,
     const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb,
     const int32_t *__restrict__ offsets, int E, int N, int K, int A, TO *__restrict__ out,
-    int kc_max, float *__restrict__ part, const StreamFuse fz) {
+    int max_pieces, float *__restrict__ part, const StreamFuse fz) {
     constexpr int P = kSP, G = kSGroups;
     constexpr int kCols = SWIGLU ? kSRowsT / 2 : kSRowsT;  // output columns per tile
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -194,13 +194,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // Work split.  Whole tiles, workgroup b taking the run of tiles
     // [b tiles / NG, (b + 1) tiles / NG) (a run of neighbouring column tiles
     // of one expert streams 3 % faster on MI355X than tiles dealt round
-    // robin); or, where the launcher allows it (kc_max > 1: scratch for the
+    // robin); or, where the launcher allows it (max_pieces > 1: scratch for the
     // partial sums is there) and whole tiles would leave CUs idle for much of
     // the kernel (few tiles, or a last round mostly empty), an even split of all
     // R = tiles x n_kr K ranges in tile order: workgroup b of the NGe used
     // walks ranges [b R / NGe, (b + 1) R / NGe), cut at tile boundaries into
-    // items.  A tile's pieces (at most kc_max: NGe is kept small enough that
-    // every workgroup gets at least (n_kr - 1) / (kc_max - 1) ranges) leave
+    // items.  A tile's pieces (at most max_pieces: NGe is kept small enough that
+    // every workgroup gets at least (n_kr - 1) / (max_pieces - 1) ranges) leave
     // fp32 partial sums, summed in K order by stream_reduce_kernel.  The
     // split is taken when it cuts the K ranges of the busiest workgroup by
     // at least 10 % (the partial sums and the extra pass cost a few
@@ -211,14 +211,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t R = (int64_t)tiles * n_kr;
     bool split = false;
     int NGe = NG;
-    if (kc_max > 1 && tiles > 0) {
-        const int s_need = n_kr > 1 ? (n_kr - 2) / (kc_max - 1) + 1 : 1;
+    if (max_pieces > 1 && tiles > 0) {
+        const int s_need = n_kr > 1 ? (n_kr - 2) / (max_pieces - 1) + 1 : 1;
         NGe = (int)max<int64_t>(1, min<int64_t>(NG, R / s_need));
         const int64_t whole = (int64_t)((tiles + NG - 1) / NG) * n_kr;
         split = 10 * ((R + NGe - 1) / NGe) <= 9 * whole;
         if (!split) NGe = NG;
     }
-    if (kc_max > 1 && blockIdx.x == 0 && tid == 0) {
+    if (max_pieces > 1 && blockIdx.x == 0 && tid == 0) {
         ((int *)part)[0] = split ? 1 : 0;
         ((int *)part)[1] = NG;
     }
@@ -682,19 +682,19 @@ int stream_layer_pieces(int64_t A, int d, int E) {
 template <bool SWIGLU, typename TO>
 hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
-                         void *out, int kc_max, float *part, hipStream_t s,
+                         void *out, int max_pieces, float *part, hipStream_t s,
                          const StreamFuse &fz = StreamFuse{}, bool reduce = true) {
     hipError_t err = set_lds_limit<stream_gemm_kernel<SWIGLU, TO>>(kSLds);
     if (err != hipSuccess) return err;
     // one workgroup per CU, never more than there can be items:
-    // sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1 tiles, kc_max items each
+    // sum_e ceil(c_e / BT) <= ceil(A / BT) + E - 1 tiles, max_pieces items each
     const int64_t cols = SWIGLU ? kSRowsT / 2 : kSRowsT;
-    const int64_t item_bound = (N + cols - 1) / cols * ((A + kSBT - 1) / kSBT + E - 1) * kc_max;
+    const int64_t item_bound = (N + cols - 1) / cols * ((A + kSBT - 1) / kSBT + E - 1) * max_pieces;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), item_bound));
     hipLaunchKernelGGL((stream_gemm_kernel<SWIGLU, TO>), dim3(grid), dim3(256), kSLds, s,
                        (const bf16_t *)act, act_ld, gather, (const bf16_t *)Wa,
-                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, kc_max, part, fz);
-    if ((err = hipGetLastError()) != hipSuccess || kc_max == 1 || !reduce) return err;
+                       (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, max_pieces, part, fz);
+    if ((err = hipGetLastError()) != hipSuccess || max_pieces == 1 || !reduce) return err;
     const int64_t n4 = A * N / 4;  // N is a multiple of 512
     const int rgrid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
     hipLaunchKernelGGL((stream_reduce_kernel<SWIGLU, TO>), dim3(rgrid), dim3(256), 0, s,
@@ -727,28 +727,28 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
                                int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
                                float *partial, size_t partial_bytes, const StreamFuse &fuse,
                                hipEvent_t gemm1_done, hipStream_t s) {
-    int kc = stream_layer_pieces(A, d, E);
-    if (kc > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) kc = 1;
+    int pieces = stream_layer_pieces(A, d, E);
+    if (pieces > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) pieces = 1;
     // GEMM1 reads token rows through the map it builds.  GEMM2 combines in
-    // its own tail where its tiles are never split (kc == 1); else the pass
+    // its own tail where its tiles are never split (pieces == 1); else the pass
     // that sums its pieces forms y.
     StreamFuse f1 = fuse;
-    f1.ctr_n = fuse.y && kc == 1 ? stream_combine_counters(d) : 0;
+    f1.ctr_n = fuse.y && pieces == 1 ? stream_combine_counters(d) : 0;
     f1.gw = nullptr;
     f1.residual = nullptr;
     f1.y = nullptr;
     hipError_t err = launch_stream<true, bf16_t>(x, d, fuse.token_of, W1, W3, fuse.offsets, E,
-                                                 d_ff, d, A, hbuf, kc, partial, s, f1);
+                                                 d_ff, d, A, hbuf, pieces, partial, s, f1);
     if (err == hipSuccess && gemm1_done) err = hipEventRecord(gemm1_done, s);
     if (err != hipSuccess) return err;
     StreamFuse f2{};
-    if (kc == 1 && fuse.y) {
+    if (pieces == 1 && fuse.y) {
         f2 = fuse;
         f2.topk_idx = nullptr;
     }
     err = launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, fuse.offsets, E, d, d_ff,
-                                      A, out, kc, partial, s, f2, !(kc > 1 && fuse.y));
-    if (err != hipSuccess || kc == 1 || !fuse.y) return err;
+                                      A, out, pieces, partial, s, f2, !(pieces > 1 && fuse.y));
+    if (err != hipSuccess || pieces == 1 || !fuse.y) return err;
     const int64_t T = fuse.T, n8 = T * d / 8;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n8 + 255) / 256));
     hipLaunchKernelGGL(stream_reduce_combine_kernel, dim3(grid), dim3(256), 0, s,
@@ -763,17 +763,17 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
                              float *partial, size_t partial_bytes, hipEvent_t mid,
                              hipStream_t s) {
     // split tiles only when the scratch for their partial sums is there
-    int kc = kSMaxPieces;
-    if (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E)) kc = 1;
+    int pieces = kSMaxPieces;
+    if (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E)) pieces = 1;
     hipError_t err = launch_stream<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A,
-                                                 hbuf, kc, partial, s);
+                                                 hbuf, pieces, partial, s);
     if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
     if (err != hipSuccess) return err;
     if (out_f32)
         return launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff,
-                                           A, out, kc, partial, s);
+                                           A, out, pieces, partial, s);
     return launch_stream<false, bf16_t>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff, A,
-                                        out, kc, partial, s);
+                                        out, pieces, partial, s);
 }
 
 }  // namespace moe
