@@ -194,8 +194,9 @@ def test_permute_is_the_oracles_stable_grouping():
     assert torch.equal(xp, xs)
 
 
-def test_permute_empty_and_skewed_groups():
-    T, E, k, d = 777, 8, 2, 128
+@pytest.mark.parametrize("T", [777, 5000])   # one workgroup; chunks over the chip
+def test_permute_empty_and_skewed_groups(T):
+    E, k, d = 8, 2, 128
     idx = torch.tensor([[3, 5]] * T, dtype=torch.int32, device=DEV)
     x = torch.randn((T, d), device=DEV).to(torch.bfloat16)
     P = moe.moe_permute(x, idx, E)
