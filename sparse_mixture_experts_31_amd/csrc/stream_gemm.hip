@@ -397,8 +397,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 ++pq;
                 // the two waves of this row group's parity, one token fragment
                 // each (the fragment reads run RD k-steps ahead of the MFMAs,
-                // which alternate between two accumulators)
-                if ((RG & 1) == par) {
+                // which alternate between two accumulators); a fragment past
+                // the tile's rows would only multiply padding, so its wave
+                // skips the reads and MFMAs (its outputs are never stored)
+                if ((RG & 1) == par && 16 * jfrag < cti.mrem) {
                     constexpr int NT = kSKRange / 32, RD = 3;
                     const char *wslot = wring + ((s0 + RG) % P) * kSWStage;
                     i32x4 w[NT], x[NT];
