@@ -238,8 +238,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int my_items = 0;
     if (split)
         my_items = ((int)blockIdx.x < NGe) ? (g1 - 1) / n_kr - t_first + 1 : 0;
-    const int tw0 = (int)((int64_t)blockIdx.x * tiles / NG);
-    const int tw1 = (int)(((int64_t)blockIdx.x + 1) * tiles / NG);
+    // Whole tiles: workgroup b runs on XCD b % 8, so the runs are numbered
+    // XCD by XCD (bx) and each XCD's L2 holds one stretch of tiles, whose
+    // token rows and expert are mostly shared, rather than every eighth run.
+    const int bx = (NG % 8 == 0) ? ((int)blockIdx.x % 8) * (NG / 8) + (int)blockIdx.x / 8
+                                 : (int)blockIdx.x;
+    const int tw0 = (int)((int64_t)bx * tiles / NG);
+    const int tw1 = (int)(((int64_t)bx + 1) * tiles / NG);
     if (!split)
         my_items = tw1 - tw0;
     if (my_items == 0) return;  // uniform over the workgroup
