@@ -77,8 +77,12 @@ size_t moe_workspace_size(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt
  * moe_expert_ffn and moe_block_forward for this shape (the choice depends on
  * the average rows per expert, T*k/E, on dt and on d, d_ff): one of
  * "stream_gemm_kernel", "skinny_gemm_kernel", "grouped_gemm_kernel (...)",
- * "wide_gemm_kernel (...)".  Static storage; "" for shapes the library
- * rejects.  Host only, enqueues nothing. */
+ * "wide_gemm_kernel (...)".  Where this names "stream_gemm_kernel" and T is
+ * 1 to 4 with T*k <= 32 (and, on 256 CUs, d <= 32768 and d_ff <= 16384),
+ * moe_forward and moe_block_forward run the layer's expert GEMMs on
+ * "stream_cols_kernel" instead (each workgroup streams its own columns of
+ * every active expert); moe_expert_ffn keeps the former.  Static storage;
+ * "" for shapes the library rejects.  Host only, enqueues nothing. */
 const char *moe_expert_ffn_kernels(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt);
 
 /* Router: scores, top-k and gates for T tokens.

@@ -142,6 +142,20 @@ __device__ __forceinline__ void dma16_nt(const char *g, char *lds) {
                                      2 /* nt */);
 }
 
+// One dword per lane (256 bytes per wave): a load that only keeps a wave's
+// count of loads in flight the same from stage to stage (into LDS nothing
+// reads, from an address the caches hold).
+__device__ __forceinline__ void dma4(const char *g, char *lds) {
+    __builtin_amdgcn_global_load_lds((const void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+}
+
+// Byte offset of 16-byte chunk c of 1 KiB row r in a buffer of such rows
+// (the weight-streaming kernels' layout): chunk c of row r sits at chunk
+// c ^ (r & 15), so sixteen rows read at one chunk hit sixteen bank groups
+// while every load instruction still writes one contiguous row piece.
+__device__ __forceinline__ int swz1k(int r, int c) { return r * 1024 + ((c ^ (r & 15)) << 4); }
+
 // Activation row of the expert-order rows rb + lane / (64 / ROWS) (the rows
 // one load instruction covers), rows past `last` repeating `last`.  With a
 // gather map (the token of each expert-order row) the rows are the tokens'
@@ -235,6 +249,14 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
 // combine into GEMM2 or the pass after it (out: fp32 expert outputs).  act
 // is x (rows read in place); offsets receives the grouping (fuse.offsets).
 int stream_combine_counters(int d);
+// The decode layer's experts for one to four tokens (stream_cols.hip):
+// every workgroup streams its own columns of every active expert over the
+// whole K; GEMM1 writes h and the grouping (fuse.counts, offsets, row_of,
+// token_of), GEMM2 writes y (fuse.gw, residual, y, T, k, topk_idx).
+bool stream_cols_supported(int64_t T, int k, int d, int d_ff, int E);
+hipError_t launch_stream_cols(const void *x, const void *W1, const void *W3, const void *W2,
+                              int64_t T, int d, int d_ff, int E, void *hbuf,
+                              const StreamFuse &f, hipEvent_t gemm1_done, hipStream_t s);
 hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, const void *W2,
                                int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
                                float *partial, size_t partial_bytes, const StreamFuse &fuse,

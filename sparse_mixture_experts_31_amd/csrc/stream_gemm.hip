@@ -69,9 +69,6 @@ constexpr int vm_allow(int rg) {
 }
 static_assert(vm_allow(4) < 64, "vmcnt range");
 
-// Byte offset of 16-byte chunk c of 1 KiB row r in a buffer of such rows.
-__device__ __forceinline__ int swz1k(int r, int c) { return r * 1024 + ((c ^ (r & 15)) << 4); }
-
 }  // namespace
 
 template <bool SWIGLU, typename TO>
@@ -734,6 +731,10 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
                                int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
                                float *partial, size_t partial_bytes, const StreamFuse &fuse,
                                hipEvent_t gemm1_done, hipStream_t s) {
+    // one to four tokens: each workgroup streams its own columns of every
+    // active expert (stream_cols.hip), no split tiles, GEMM2 forms y
+    if (fuse.y && stream_cols_supported(fuse.T, fuse.k, d, d_ff, E))
+        return launch_stream_cols(x, W1, W3, W2, fuse.T, d, d_ff, E, hbuf, fuse, gemm1_done, s);
     int pieces = stream_layer_pieces(A, d, E);
     if (pieces > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) pieces = 1;
     // GEMM1 reads token rows through the map it builds.  GEMM2 combines in

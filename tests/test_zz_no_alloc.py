@@ -22,6 +22,8 @@ DEV = "cuda"
     # mid-sized grouped tiles and fp32
     Workload("noalloc-grouped", 50, T=150, d=512, d_ff=1024),
     Workload("noalloc-f32", 51, T=64, d=256, d_ff=448, dtype="f32"),
+    # four tokens, then one: the column kernels
+    Workload("noalloc-few-tokens", 52, T=4, d=1024, d_ff=2048),
 ], ids=lambda w: w.name)
 def test_noalloc_forward_matches_moe_forward(w):
     log(f"case {w.name}: T={w.T} d={w.d} d_ff={w.d_ff} {w.dtype}")
