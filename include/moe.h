@@ -78,7 +78,8 @@ size_t moe_workspace_size(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt
  * the average rows per expert, T*k/E, on dt and on d, d_ff): one of
  * "stream_gemm_kernel", "skinny_gemm_kernel", "grouped_gemm_kernel (...)",
  * "wide_gemm_kernel (...)".  Where this names "stream_gemm_kernel" and T is
- * 1 to 4 with T*k <= 32 (and, on 256 CUs, d <= 32768 and d_ff <= 16384),
+ * 1 to 8 with T*k <= 32 (and, on 256 CUs, d_ff <= 16384 and d <= 32768 for
+ * up to 4 tokens, d <= 16384 for 5 to 8),
  * moe_forward and moe_block_forward run the layer's expert GEMMs on
  * "stream_cols_kernel" instead (each workgroup streams its own columns of
  * every active expert); moe_expert_ffn keeps the former.  Static storage;

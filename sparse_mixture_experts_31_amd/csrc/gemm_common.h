@@ -249,7 +249,7 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
 // combine into GEMM2 or the pass after it (out: fp32 expert outputs).  act
 // is x (rows read in place); offsets receives the grouping (fuse.offsets).
 int stream_combine_counters(int d);
-// The decode layer's experts for one to four tokens (stream_cols.hip):
+// The decode layer's experts for one to eight tokens (stream_cols.hip):
 // every workgroup streams its own columns of every active expert over the
 // whole K; GEMM1 writes h and the grouping (fuse.counts, offsets, row_of,
 // token_of), GEMM2 writes y (fuse.gw, residual, y, T, k, topk_idx).

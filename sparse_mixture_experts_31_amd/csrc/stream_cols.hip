@@ -1,13 +1,13 @@
 // stream_cols.hip — the decode layer's expert GEMMs for the smallest
-// batches (one to four tokens, so at most four rows per expert).
+// batches (one to eight tokens, so at most eight rows per expert).
 //
 // Same experts and the same weight stream as stream_gemm.hip (the SwiGLU
 // MLP W2 (silu(W1 x) * W3 x): fdeinterviews breakdown, "The paper in one
 // minute"; tokentrails lineage, Code listing), with the work cut the other
-// way.  One to four tokens keep only a few experts busy (two for one token
-// under top-2), and the tile kernel's 128-row tiles of so few experts cannot
-// give every CU an even share: it cuts their K into pieces whose fp32 partial
-// sums need a pass of their own after each GEMM.  Here workgroup b owns a
+// way.  A few tokens keep only a few experts busy (two for one token under
+// top-2) with a few rows each, and the tile kernel's 128-row tiles of them
+// cannot give every CU an even share: it cuts their K into pieces whose fp32
+// partial sums need a pass of their own after each GEMM.  Here workgroup b owns a
 // run of output columns of every active expert and streams those weight rows
 // over the whole K, so every CU streams the same bytes and nothing is left to
 // add up afterwards:
@@ -23,8 +23,8 @@
 // and 1 GEMM2 stage per active expert on every CU).  The ring is the tile
 // kernel's: five 16 KiB slots, every weight row piece one non-temporal
 // global_load_lds, every wave issuing the same number of loads per stage (4
-// weight rows and one token row or a dword into LDS nothing reads) so each
-// wait is one constant.  A slot is refilled only once every wave is past
+// weight rows, and one or two token rows or as many dwords into LDS nothing
+// reads) so each wait is one constant.  A slot is refilled only once every wave is past
 // it, so the time a stage's compute takes after its data lands is bytes
 // not in flight: all four waves compute every stage, a quarter of its K
 // each (4 v_mfma_f32_16x16x32_bf16; four of the sixteen token columns are
@@ -38,22 +38,34 @@ namespace moe {
 
 namespace {
 
-constexpr int kCTok = 4;       // token rows per expert at most (a token picks an expert once)
-constexpr int kCMaxS = 8;      // stages per expert and K range on one workgroup, at most
 constexpr int kCP = 5;         // stages in the ring
 constexpr int kCTB = 5;        // token buffers, one per (expert, K range) in flight
 constexpr int kCAMax = 32;     // assignments T k at most
 constexpr int kCStage = 16 * 1024;
-constexpr int kCTokBuf = kCTok * 1024;
-constexpr int kCOCols = kCMaxS * 16;  // GEMM2 output columns of one workgroup, at most
-constexpr int kCLoads = 5;     // loads per wave per stage
-constexpr int kCRed = kCMaxS * 4 * kWave * 16;  // the waves' partial sums of a stage set
-constexpr int kCLds = kCP * kCStage + kCTB * kCTokBuf + 1024 + kCAMax * kCOCols * 4 + kCRed;
-static_assert(kCLds <= 160 * 1024 - 2 * 1024, "LDS capacity (2 KiB of static tables)");
 // A token buffer is reloaded kCTB K ranges (at least kCTB stages) after it
 // was first read, with the load of a stage P - 1 ahead of the consumer: the
 // stages reading it are done by then when kCTB >= P.
 static_assert(kCTB >= kCP, "token buffer reuse");
+
+// Sizes for TOK token rows per expert at most (TOK = 4 for one to four
+// tokens, 8 for five to eight: a token picks an expert once).  Each wave
+// loads TOK / 4 of an expert's token rows with the first stage of its K
+// range and as many dwords into `junk` with the others, so every stage
+// issues LOADS loads per wave.  GEMM2 at TOK = 8 takes at most four column
+// stages per workgroup, to stay within LDS with the larger token buffers.
+template <bool SWIGLU, int TOK>
+struct ColsCfg {
+    static constexpr int kTokLoads = TOK / 4;
+    static constexpr int kLoads = 4 + kTokLoads;
+    static constexpr int kCPS = SWIGLU ? 8 : 16;  // output columns per stage
+    static constexpr int kMaxS = (SWIGLU || TOK == 4) ? 8 : 4;  // column stages per workgroup
+    static constexpr int kOCols = SWIGLU ? 0 : kMaxS * 16;  // GEMM2 outputs kept per assignment
+    static constexpr int kTokBuf = TOK * 1024;
+    static constexpr int kRed = kMaxS * 4 * kWave * 16;  // the waves' partial sums of a stage set
+    static constexpr int kLds = kCP * kCStage + kCTB * kTokBuf + 1024 + kCAMax * kOCols * 4 + kRed;
+    static_assert(TOK == 4 || TOK == 8, "token rows per expert");
+    static_assert(kLds <= 160 * 1024 - 2 * 1024, "LDS capacity (2 KiB of static tables)");
+};
 
 }  // namespace
 
@@ -63,23 +75,24 @@ static_assert(kCTB >= kCP, "token buffer reuse");
 // = h [T k][act_ld], Wa = W2 [E][N][K] (N = d, K = d_ff), y [T][N] receives
 // the combined output.  topk_idx [T k] holds the experts of every (token,
 // slot); out-of-range entries are skipped.  N is a multiple of 512 (16 for
-// the stages), K a multiple of 512, T k <= kCAMax, E <= 64, and the grid
-// leaves each workgroup between 1 and kCMaxS stages of columns.
-template <bool SWIGLU>
+// the stages), K a multiple of 512, T k <= kCAMax, E <= 64, every expert has
+// at most TOK rows, and the grid leaves each workgroup between 1 and
+// ColsCfg::kMaxS stages of columns.
+template <bool SWIGLU, int TOK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void stream_cols_kernel(
     const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ topk_idx, int k,
     int T, const bf16_t *__restrict__ Wa, const bf16_t *__restrict__ Wb, int E, int N, int K,
     bf16_t *__restrict__ h, const float *__restrict__ gw, const bf16_t *__restrict__ residual,
     bf16_t *__restrict__ y, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ row_of, int32_t *__restrict__ token_of) {
-    constexpr int P = kCP;
-    constexpr int CPS = SWIGLU ? 8 : 16;  // output columns per stage
+    using C = ColsCfg<SWIGLU, TOK>;
+    constexpr int P = kCP, CPS = C::kCPS, MAXS = C::kMaxS, TL = C::kTokLoads;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     char *const ring = smem;
     char *const tbuf = smem + P * kCStage;
-    char *const junk = tbuf + kCTB * kCTokBuf;
+    char *const junk = tbuf + kCTB * C::kTokBuf;
     float *const s_o = (float *)(junk + 1024);  // GEMM2: [assignment][column] outputs
-    char *const red = (char *)(s_o + kCAMax * kCOCols);  // [stage][wave] partial sums
+    char *const red = (char *)(s_o + kCAMax * C::kOCols);  // [stage][wave] partial sums
     __shared__ int s_cnt[64], s_off[64], s_act[64], s_row[kCAMax], s_asg[kCAMax], s_nact;
 
     const int tid = threadIdx.x;
@@ -146,18 +159,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // Per-expert values, lane i for active expert i (built once, read with
     // readlane, so a stage's addresses never wait on LDS): the byte offset
-    // of its weight matrix, of the token row this wave loads for it (rows
-    // past its count repeat its last), its first grouped row and its count.
-    int64_t t_w = 0, t_tok = 0;
+    // of its weight matrix, of the token rows TL wave + j this wave loads for
+    // it (rows past its count repeat its last), its first grouped row and
+    // its count.
+    int64_t t_w = 0, t_tok[TL];
     int t_off = 0, t_cnt = 0;
+#pragma unroll
+    for (int j = 0; j < TL; ++j) t_tok[j] = 0;
     if (lane < n_act) {
         const int e = s_act[lane];
         t_off = s_off[e];
         t_cnt = s_cnt[e];
-        const int g = t_off + min(wave, t_cnt - 1);
-        const int row = SWIGLU ? s_asg[g] / k : g;
         t_w = (int64_t)e * N * K * 2;
-        t_tok = (int64_t)row * act_ld * 2;
+#pragma unroll
+        for (int j = 0; j < TL; ++j) {
+            const int g = t_off + min(TL * wave + j, t_cnt - 1);
+            const int row = SWIGLU ? s_asg[g] / k : g;
+            t_tok[j] = (int64_t)row * act_ld * 2;
+        }
     }
     auto lane64 = [](int64_t v, int i) -> int64_t {
         const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, i);
@@ -188,14 +207,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 dma16_nt(src + (lofs ^ (r << 4)), slot + r * 1024);
             }
             if (ps == 0) {
-                const char *src = (const char *)act + lane64(t_tok, pi) + pkc * 1024;
-                dma16(src + (lofs ^ (wave << 4)), tbuf + (pt % kCTB) * kCTokBuf + wave * 1024);
+#pragma unroll
+                for (int j = 0; j < TL; ++j) {
+                    const int jr = TL * wave + j;  // token row in the buffer
+                    const char *src = (const char *)act + lane64(t_tok[j], pi) + pkc * 1024;
+                    dma16(src + (lofs ^ (jr << 4)), tbuf + (pt % kCTB) * C::kTokBuf + jr * 1024);
+                }
             } else {
-                dma4(dummy, junk);
+#pragma unroll
+                for (int j = 0; j < TL; ++j) dma4(dummy, junk);
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < kCLoads; ++q) dma4(dummy, junk);
+            for (int q = 0; q < C::kLoads; ++q) dma4(dummy, junk);
         }
         ++pq;
         if (++ps == S) {
@@ -215,19 +239,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // ---- consumer: every wave computes a quarter of every stage's K
         // (k-steps 4 wave .. + 4 of the sixteen), into its own accumulators
         const int lr = lane & 15, lq = lane >> 4;
-        f32x4 acc[kCMaxS];
+        f32x4 acc[MAXS];
 #pragma unroll
-        for (int s = 0; s < kCMaxS; ++s) acc[s] = f32x4{};
+        for (int s = 0; s < MAXS; ++s) acc[s] = f32x4{};
         int cq = 0;  // stages consumed
         for (int i = 0; i < n_act; ++i) {
             for (int kc = 0; kc < n_kc; ++kc) {
-                const char *tb = tbuf + ((i * n_kc + kc) % kCTB) * kCTokBuf;
+                const char *tb = tbuf + ((i * n_kc + kc) % kCTB) * C::kTokBuf;
 #pragma unroll
-                for (int s = 0; s < kCMaxS; ++s) {
+                for (int s = 0; s < MAXS; ++s) {
                     if (s < S) {
                         // stage cq landed (this wave's loads, then everyone's),
                         // and every wave is done with the slot loaded next
-                        wait_vmcnt_lgkm0<(P - 2) * kCLoads>();
+                        wait_vmcnt_lgkm0<(P - 2) * C::kLoads>();
                         stage_barrier();
                         issue();
                         constexpr int NT = 4;
@@ -237,7 +261,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         for (int t = 0; t < NT; ++t) {
                             const int c = 4 * (NT * wave + t) + lq;
                             w[t] = *(const i32x4 *)(ws + swz1k(lr, c));
-                            xv[t] = *(const i32x4 *)(tb + swz1k(lr & (kCTok - 1), c));
+                            xv[t] = *(const i32x4 *)(tb + swz1k(lr & (TOK - 1), c));
                         }
                         f32x4 ab[2] = {acc[s], f32x4{}};
 #pragma unroll
@@ -254,7 +278,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             // (tokens below the expert's count are real); GEMM1: rows 0-7
             // are u, rows 8-15 the same columns' v, 32 lanes apart.
 #pragma unroll
-            for (int s = 0; s < kCMaxS; ++s) {
+            for (int s = 0; s < MAXS; ++s) {
                 if (s < S) *(f32x4 *)(red + ((s * 4 + wave) * kWave + lane) * 16) = acc[s];
                 acc[s] = f32x4{};
             }
@@ -267,7 +291,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int s = wave + 4 * hh;
-                if (s < S) {
+                if (s < S && s < MAXS) {
                     f32x4 x = *(const f32x4 *)(red + ((s * 4 + 0) * kWave + lane) * 16);
 #pragma unroll
                     for (int ww = 1; ww < 4; ++ww)
@@ -286,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         }
                     } else if (n < cnt) {
                         const int a = s_asg[off + n];
-                        *(f32x4 *)(s_o + a * kCOCols + CPS * s + 4 * lq) = x;
+                        *(f32x4 *)(s_o + a * C::kOCols + CPS * s + 4 * lq) = x;
                     }
                 }
             }
@@ -309,7 +333,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 const int a = t * k + j;
                 if (s_row[a] < 0) continue;
                 const float g = gw[a];
-                const float *o = s_o + a * kCOCols + cl;
+                const float *o = s_o + a * C::kOCols + cl;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc8[c] = fmaf(g, o[c], acc8[c]);
             }
@@ -336,33 +360,55 @@ namespace {
 // Workgroups of each GEMM: one per CU, never more than its stages of columns.
 int cols_grid(int stages) { return std::max(1, std::min(device_cus(), stages)); }
 
+// Token rows per expert the kernels are built for at T tokens (0: none).
+int cols_tok(int64_t T) { return T < 1 ? 0 : T <= 4 ? 4 : T <= 8 ? 8 : 0; }
+
+template <int TOK>
+hipError_t launch_cols(const void *x, const void *W1, const void *W3, const void *W2, int64_t T,
+                       int d, int d_ff, int E, void *hbuf, const StreamFuse &f,
+                       hipEvent_t gemm1_done, hipStream_t s) {
+    using C1 = ColsCfg<true, TOK>;
+    using C2 = ColsCfg<false, TOK>;
+    hipError_t err = set_lds_limit<stream_cols_kernel<true, TOK>>(C1::kLds);
+    if (err == hipSuccess) err = set_lds_limit<stream_cols_kernel<false, TOK>>(C2::kLds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((stream_cols_kernel<true, TOK>), dim3(cols_grid(d_ff / C1::kCPS)), dim3(256),
+                       C1::kLds, s, (const bf16_t *)x, (int64_t)d, f.topk_idx, f.k, (int)T,
+                       (const bf16_t *)W1, (const bf16_t *)W3, E, d_ff, d, (bf16_t *)hbuf,
+                       nullptr, nullptr, nullptr, f.counts, f.offsets, f.row_of, f.token_of);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (gemm1_done && (err = hipEventRecord(gemm1_done, s)) != hipSuccess) return err;
+    hipLaunchKernelGGL((stream_cols_kernel<false, TOK>), dim3(cols_grid(d / C2::kCPS)), dim3(256),
+                       C2::kLds, s, (const bf16_t *)hbuf, (int64_t)d_ff, f.topk_idx, f.k, (int)T,
+                       (const bf16_t *)W2, nullptr, E, d, d_ff, nullptr, f.gw, f.residual, f.y,
+                       nullptr, nullptr, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+template <int TOK>
+bool cols_fit(int d, int d_ff) {
+    using C1 = ColsCfg<true, TOK>;
+    using C2 = ColsCfg<false, TOK>;
+    const int s1 = d_ff / C1::kCPS, s2 = d / C2::kCPS;
+    const int g1 = cols_grid(s1), g2 = cols_grid(s2);
+    return (s1 + g1 - 1) / g1 <= C1::kMaxS && (s2 + g2 - 1) / g2 <= C2::kMaxS;
+}
+
 }  // namespace
 
 bool stream_cols_supported(int64_t T, int k, int d, int d_ff, int E) {
-    if (T < 1 || T > kCTok || T * k > kCAMax || E < 1 || E > 64) return false;
+    const int tok = cols_tok(T);
+    if (tok == 0 || T * k > kCAMax || E < 1 || E > 64) return false;
     if (d < 512 || d_ff < 512 || d % 512 != 0 || d_ff % 512 != 0) return false;
-    const int s1 = d_ff / 8, s2 = d / 16;
-    const int g1 = cols_grid(s1), g2 = cols_grid(s2);
-    return (s1 + g1 - 1) / g1 <= kCMaxS && (s2 + g2 - 1) / g2 <= kCMaxS;
+    return tok == 4 ? cols_fit<4>(d, d_ff) : cols_fit<8>(d, d_ff);
 }
 
 hipError_t launch_stream_cols(const void *x, const void *W1, const void *W3, const void *W2,
                               int64_t T, int d, int d_ff, int E, void *hbuf,
                               const StreamFuse &f, hipEvent_t gemm1_done, hipStream_t s) {
-    hipError_t err = set_lds_limit<stream_cols_kernel<true>>(kCLds);
-    if (err == hipSuccess) err = set_lds_limit<stream_cols_kernel<false>>(kCLds);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((stream_cols_kernel<true>), dim3(cols_grid(d_ff / 8)), dim3(256), kCLds, s,
-                       (const bf16_t *)x, (int64_t)d, f.topk_idx, f.k, (int)T, (const bf16_t *)W1,
-                       (const bf16_t *)W3, E, d_ff, d, (bf16_t *)hbuf, nullptr, nullptr, nullptr,
-                       f.counts, f.offsets, f.row_of, f.token_of);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (gemm1_done && (err = hipEventRecord(gemm1_done, s)) != hipSuccess) return err;
-    hipLaunchKernelGGL((stream_cols_kernel<false>), dim3(cols_grid(d / 16)), dim3(256), kCLds, s,
-                       (const bf16_t *)hbuf, (int64_t)d_ff, f.topk_idx, f.k, (int)T,
-                       (const bf16_t *)W2, nullptr, E, d, d_ff, nullptr, f.gw, f.residual, f.y,
-                       nullptr, nullptr, nullptr, nullptr);
-    return hipGetLastError();
+    if (cols_tok(T) == 4)
+        return launch_cols<4>(x, W1, W3, W2, T, d, d_ff, E, hbuf, f, gemm1_done, s);
+    return launch_cols<8>(x, W1, W3, W2, T, d, d_ff, E, hbuf, f, gemm1_done, s);
 }
 
 }  // namespace moe

@@ -731,7 +731,7 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
                                int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
                                float *partial, size_t partial_bytes, const StreamFuse &fuse,
                                hipEvent_t gemm1_done, hipStream_t s) {
-    // one to four tokens: each workgroup streams its own columns of every
+    // one to eight tokens: each workgroup streams its own columns of every
     // active expert (stream_cols.hip), no split tiles, GEMM2 forms y
     if (fuse.y && stream_cols_supported(fuse.T, fuse.k, d, d_ff, E))
         return launch_stream_cols(x, W1, W3, W2, fuse.T, d, d_ff, E, hbuf, fuse, gemm1_done, s);

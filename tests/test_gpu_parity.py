@@ -72,14 +72,14 @@ SMALL = [
     # taking all eight experts
     Workload("e1-k1", 27, T=50, d=256, d_ff=512, E=1, k=1),
     Workload("k-all", 28, T=40, d=256, d_ff=256, E=8, k=8),
-    # the weight stream's even K split with few tiles (from five tokens on;
+    # the weight stream's even K split with few tiles (from nine tokens on;
     # fewer go to the column kernels below): GEMM1 8 tiles of 8 K ranges on
     # 64 workgroups (8 pieces a tile) ...
-    Workload("split-8-pieces", 29, T=5, d=4096, d_ff=512, E=1, k=1),
+    Workload("split-8-pieces", 29, T=9, d=4096, d_ff=512, E=1, k=1),
     # ... GEMM2 8 tiles of 14 K ranges on 56 workgroups (7 pieces a tile)
-    Workload("split-7-pieces", 30, T=5, d=512, d_ff=7168, E=2, k=1),
+    Workload("split-7-pieces", 30, T=9, d=512, d_ff=7168, E=2, k=1),
     # ... both GEMMs split, pieces of 1-3 ranges crossing tile boundaries
-    Workload("split-5-tokens", 31, T=5, d=1024, d_ff=3584, E=8, k=2),
+    Workload("split-9-tokens", 31, T=9, d=1024, d_ff=3584, E=8, k=2),
     # ... and in a layer of two experts with 24 rows each, where GEMM2 has 16
     # tiles (whole tiles would leave most CUs idle)
     Workload("split-two-experts", 32, T=24, d=1024, d_ff=2048, E=2, k=2),
@@ -100,6 +100,17 @@ SMALL = [
     # GEMM2 (d = 32768, 64 K ranges in GEMM1), then GEMM1 (d_ff = 16384)
     Workload("cols-eight-stages-w2", 39, T=1, d=32768, d_ff=512, E=2, k=1),
     Workload("cols-eight-stages-w13", 40, T=2, d=512, d_ff=16384, E=2, k=1),
+    # five to eight tokens: eight token rows per expert at most, two per wave
+    Workload("cols-eight-tokens", 41, T=8, d=1024, d_ff=3584, E=8, k=2),
+    Workload("cols-six-rows-e1", 43, T=6, d=512, d_ff=1024, E=1, k=1),
+    Workload("cols-tok8-e64-k4", 44, T=8, d=512, d_ff=1024, E=64, k=4),
+    # ... GEMM2 two and four stages per workgroup (its most at eight rows),
+    # GEMM1 eight
+    Workload("cols-tok8-two-stages", 45, T=7, d=8192, d_ff=512, E=4, k=2),
+    Workload("cols-tok8-four-stages", 46, T=5, d=16384, d_ff=512, E=2, k=1),
+    Workload("cols-tok8-eight-stages-w13", 47, T=6, d=512, d_ff=16384, E=2, k=1),
+    # ... and past four GEMM2 stages the tile kernel takes the layer again
+    Workload("cols-tok8-too-wide", 48, T=5, d=32768, d_ff=512, E=2, k=1),
 ]
 
 
@@ -411,8 +422,8 @@ def test_runs_are_bit_identical():
     assert torch.equal(y1, y2)
 
 
-@pytest.mark.parametrize("name", ["stream-tiles", "split-5-tokens", "cols-three-tokens",
-                                  "grouped-bf16", "wide-narrow"])
+@pytest.mark.parametrize("name", ["stream-tiles", "split-9-tokens", "cols-three-tokens",
+                                  "cols-eight-tokens", "grouped-bf16", "wide-narrow"])
 def test_side_streams_give_the_default_streams_result(name):
     """moe_forward on two side streams at once, each with its own output and
     workspace, matches the default stream's result bit for bit: every launch
@@ -437,8 +448,8 @@ def test_side_streams_give_the_default_streams_result(name):
         assert torch.equal(y, y0)
 
 
-@pytest.mark.parametrize("name", ["stream-tiles", "split-5-tokens", "cols-three-tokens",
-                                  "grouped-bf16", "wide-narrow"])
+@pytest.mark.parametrize("name", ["stream-tiles", "split-9-tokens", "cols-three-tokens",
+                                  "cols-eight-tokens", "grouped-bf16", "wide-narrow"])
 def test_layer_replays_from_a_hip_graph(name):
     """moe_forward captured once in a HIP graph (no allocation, memset or
     synchronisation inside the layer) and replayed on new inputs copied into
@@ -553,13 +564,14 @@ def test_stack_small():
     _stack_check(w, blocks, h0, np.arange(w.T))
 
 
-@pytest.mark.parametrize("T", [32, 8, 3])
+@pytest.mark.parametrize("T", [32, 12, 8, 3])
 def test_stack_decode_sized(T):
     """Decoder blocks at decode sizes run on the weight-streaming kernels,
     where GEMM1 groups the assignments itself and (from four rows per
-    expert on, T = 32 here) GEMM2 forms h + y in place; T = 8 keeps the
-    pass that sums split tiles and combines; T = 3 runs the column kernels,
-    whose GEMM2 forms h + y itself."""
+    expert on, T = 32 here) GEMM2 forms h + y in place; T = 12 keeps the
+    pass that sums split tiles and combines; T = 8 and 3 run the column
+    kernels (eight and four token rows per expert), whose GEMM2 forms h + y
+    itself."""
     from sparse_mixture_experts_31_amd.inputs import make_stack
     w = Workload(f"stack-decode-{T}", 42, T=T, d=1024, d_ff=2048, blocks=3)
     assert moe.moe_expert_ffn_kernels(T, w.d, w.d_ff, w.E, w.k, torch.bfloat16) == \

@@ -17,7 +17,7 @@ DEV = "cuda"
 
 
 @pytest.mark.parametrize("w", [
-    # the decode workload: T = 32, then 8 (weight stream with split tiles)
+    # the decode workload: T = 32 (whole tiles), then 8 (the column kernels)
     WORKLOADS["decode"],
     # mid-sized grouped tiles and fp32
     Workload("noalloc-grouped", 50, T=150, d=512, d_ff=1024),
