@@ -426,7 +426,7 @@ def main():
     tokens_per_s = w.T / (ms_per_step * 1e-3)
 
     counts, routing = routing_summary(w, L, moe, np, torch)
-    kernel = moe.moe_expert_ffn_kernels(w.T, w.d, w.d_ff, w.E, w.k, w.torch_dtype)
+    kernel = moe.moe_forward_kernels(w.T, w.d, w.d_ff, w.E, w.k, w.torch_dtype)
     roofline = gemm1_roofline(w, counts, gemm1_ms, kernel) if blocks is None else None
     layer = layer_roofline(w, routing["active_experts"], ms_per_step)
 
@@ -444,7 +444,7 @@ def main():
         p_ms, p_g1, p_stages = time_layer(wp, Lp, moe, np, torch, ev, stream, args.steps,
                                           args.warmup)
         p_counts, p_routing = routing_summary(wp, Lp, moe, np, torch)
-        p_kernel = moe.moe_expert_ffn_kernels(wp.T, wp.d, wp.d_ff, wp.E, wp.k, wp.torch_dtype)
+        p_kernel = moe.moe_forward_kernels(wp.T, wp.d, wp.d_ff, wp.E, wp.k, wp.torch_dtype)
         prefill = {"config": {"workload": wp.name, "T": wp.T, "d": wp.d, "d_ff": wp.d_ff,
                               "E": wp.E, "k": wp.k, "act_dtype": wp.dtype},
                    "ms_per_step": round(p_ms, 4),

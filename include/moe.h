@@ -77,14 +77,20 @@ size_t moe_workspace_size(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt
  * moe_expert_ffn and moe_block_forward for this shape (the choice depends on
  * the average rows per expert, T*k/E, on dt and on d, d_ff): one of
  * "stream_gemm_kernel", "skinny_gemm_kernel", "grouped_gemm_kernel (...)",
- * "wide_gemm_kernel (...)".  Where this names "stream_gemm_kernel" and T is
- * 1 to 8 with T*k <= 32 (and, on 256 CUs, d_ff <= 16384 and d <= 32768 for
- * up to 4 tokens, d <= 16384 for 5 to 8),
- * moe_forward and moe_block_forward run the layer's expert GEMMs on
- * "stream_cols_kernel" instead (each workgroup streams its own columns of
- * every active expert); moe_expert_ffn keeps the former.  Static storage;
- * "" for shapes the library rejects.  Host only, enqueues nothing. */
+ * "wide_gemm_kernel (...)".  For the fused layer, whose choice can differ,
+ * see moe_forward_kernels.  Static storage; "" for shapes the library
+ * rejects.  Host only, enqueues nothing. */
 const char *moe_expert_ffn_kernels(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt);
+
+/* The same for the expert GEMMs of moe_forward, moe_forward_noalloc,
+ * moe_forward_profiled and moe_block_forward at T tokens: where
+ * moe_expert_ffn_kernels names "stream_gemm_kernel" and T is 1 to 8 with
+ * T*k <= 32 (and, on 256 CUs, d_ff <= 16384, d <= 32768 up to four tokens
+ * and d <= 16384 for five to eight), the layer runs "stream_cols_kernel"
+ * (each workgroup streams its own columns of every active expert over the
+ * whole K, GEMM2 forms y); otherwise the same name.  Static storage; "" for
+ * shapes the library rejects.  Host only, enqueues nothing. */
+const char *moe_forward_kernels(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt);
 
 /* Router: scores, top-k and gates for T tokens.
  *   x [T][d] (dt), Wg fp32 [E][d]

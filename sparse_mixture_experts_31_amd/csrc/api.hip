@@ -152,6 +152,11 @@ const char *moe_expert_ffn_kernels(int64_t T, int d, int d_ff, int E, int k, moe
     return moe_expert_ffn_kernel_name((int)dt, T * k, d, d_ff, E);
 }
 
+const char *moe_forward_kernels(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt) {
+    if (check_shape(T, d, d_ff, E, k, dt, true) != MOE_OK) return "";
+    return moe_forward_kernel_name((int)dt, T, k, d, d_ff, E);
+}
+
 size_t moe_route_balance_workspace_size(int64_t T, int E) {
     if (T < 1 || E < 1 || E > 64) return 0;
     const size_t blocks = (size_t)moe_router_blocks(T);

@@ -110,6 +110,9 @@ hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k
                                    hipEvent_t gemm1_done, hipStream_t s);
 // Name of the kernel family that runs the experts for this shape.
 const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E);
+// The same for the experts of the fused layer (moe_forward and friends) at T
+// tokens, which may differ: one to eight tokens take the column kernels.
+const char *moe_forward_kernel_name(int dt, int64_t T, int k, int d, int d_ff, int E);
 // The same experts for decode-sized batches (few rows per expert).
 hipError_t moe_launch_skinny_ffn(const void *x_perm, const int32_t *offsets, const void *W1,
                                  const void *W3, const void *W2, int dt, int out_f32, int64_t A,

@@ -405,6 +405,13 @@ const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E
     return "";
 }
 
+const char *moe_forward_kernel_name(int dt, int64_t T, int k, int d, int d_ff, int E) {
+    if (moe::ffn_path(dt, T * k, d, d_ff, E) == moe::FfnPath::kStream &&
+        moe::stream_cols_supported(T, k, d, d_ff, E))
+        return "stream_cols_kernel";
+    return moe_expert_ffn_kernel_name(dt, T * k, d, d_ff, E);
+}
+
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E) {
     switch (moe::ffn_path(dt, A, d, d_ff, E)) {
         case moe::FfnPath::kWide:

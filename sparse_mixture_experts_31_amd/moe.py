@@ -49,6 +49,8 @@ def lib():
         L.moe_forward_noalloc_max_scratch.argtypes = []
         L.moe_expert_ffn_kernels.restype = ctypes.c_char_p
         L.moe_expert_ffn_kernels.argtypes = [i64, i32, i32, i32, i32, i32]
+        L.moe_forward_kernels.restype = ctypes.c_char_p
+        L.moe_forward_kernels.argtypes = [i64, i32, i32, i32, i32, i32]
         L.moe_route_balance_workspace_size.restype = sz
         L.moe_route_balance_workspace_size.argtypes = [i64, i32]
         L.moe_permute_workspace_size.restype = sz
@@ -147,6 +149,12 @@ def moe_expert_ffn_kernels(T, d, d_ff, E, k, dtype) -> str:
     """Kernel family the library picks for the expert GEMMs of this shape."""
     dt = MOE_F32 if dtype in (torch.float32, MOE_F32) else MOE_BF16
     return lib().moe_expert_ffn_kernels(T, d, d_ff, E, k, dt).decode()
+
+
+def moe_forward_kernels(T, d, d_ff, E, k, dtype) -> str:
+    """Kernel family of the fused layer's expert GEMMs at T tokens."""
+    dt = MOE_F32 if dtype in (torch.float32, MOE_F32) else MOE_BF16
+    return lib().moe_forward_kernels(T, d, d_ff, E, k, dt).decode()
 
 
 def workspace(T, d, d_ff, E, k, dtype, device="cuda") -> torch.Tensor:

@@ -88,6 +88,30 @@ def test_kernel_family_labels_follow_rows_per_expert():
     assert f(8, E=65) == ""
 
 
+def test_layer_kernel_labels_name_the_column_kernels_up_to_eight_tokens():
+    """The fused layer takes the column kernels for one to eight tokens where
+    the expert FFN alone would take the tile kernel, within their LDS limits
+    (at most eight GEMM1 stages per workgroup, and eight GEMM2 stages up to
+    four tokens, four from five to eight, on 256 CUs)."""
+    f = lambda T, d=4096, d_ff=14336, E=8, k=2: moe.moe_forward_kernels(T, d, d_ff, E, k,
+                                                                        moe.MOE_BF16)
+    g = lambda T, d=4096, d_ff=14336, E=8, k=2: moe.moe_expert_ffn_kernels(T, d, d_ff, E, k,
+                                                                           moe.MOE_BF16)
+    for T in range(1, 9):
+        assert f(T) == "stream_cols_kernel" and g(T) == "stream_gemm_kernel"
+    assert f(9) == f(99) == "stream_gemm_kernel"
+    assert f(100) == g(100) and f(4096) == g(4096)
+    assert f(4, E=64, k=8) == "stream_cols_kernel"       # 32 assignments, the most
+    assert f(5, E=64, k=8) == "stream_gemm_kernel"       # 40
+    assert f(4, d=32768) == "stream_cols_kernel"         # GEMM2: 8 stages per workgroup
+    assert f(5, d=32768) == "stream_gemm_kernel"         # more than 4 at five tokens
+    assert f(8, d_ff=16384) == "stream_cols_kernel"      # GEMM1: 8 stages
+    assert f(1, d_ff=16896) == "stream_gemm_kernel"      # 9 would be needed
+    assert moe.moe_forward_kernels(4, 4096, 14336, 8, 2, moe.MOE_F32) == \
+        moe.moe_expert_ffn_kernels(4, 4096, 14336, 8, 2, moe.MOE_F32)
+    assert f(8, E=65) == ""
+
+
 def _rc(name, *args):
     return getattr(moe.lib(), name)(*args)
 
