@@ -175,12 +175,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (wave == 0) build_expert_table(s_goff, E, A, kSBT, col_tiles, s_lo, s_cnt, s_first);
     } else if (wave == 0) {
         build_expert_table(offsets, E, A, kSBT, col_tiles, s_lo, s_cnt, s_first);
-    } else if (gather) {
+    } else if (gather || (!SWIGLU && fz.y)) {
+        // the token map; or, for GEMM2 forming y (no map to read), row_of,
+        // which the combine in its tail looks up for every (token, slot)
+        const int32_t *src = gather ? gather : fz.row_of;
         constexpr int kStride = 256 - kWave;
         for (int i0 = tid - kWave; i0 < A; i0 += 4 * kStride) {
             int v[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = i0 + q * kStride < A ? gather[i0 + q * kStride] : 0;
+            for (int q = 0; q < 4; ++q) v[q] = i0 + q * kStride < A ? src[i0 + q * kStride] : 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (i0 + q * kStride < A) s_map[i0 + q * kStride] = v[q];
@@ -511,42 +514,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                     __HIP_MEMORY_SCOPE_AGENT) == per_block - 1;
                 __syncthreads();
                 if (s_done) {
+                    // Two 8-column pieces per thread and pass, every load of
+                    // both issued before either is summed (row_of from LDS):
+                    // one memory round trip per pass.
                     constexpr int kC8 = kCols / 8;  // 8-column pieces of a block
-                    for (int q = tid; q < fz.T * kC8; q += 256) {
-                        const int t = q / kC8;
-                        const int n = cb * kCols + (q - t * kC8) * 8;
-                        if (n >= N) continue;
-                        float acc8[8];
+                    const int n_items = fz.T * kC8;
+                    for (int q0 = tid; q0 < n_items; q0 += 512) {
+                        uint64_t ov[2][8][4];
+                        float gv[2][8];
+                        int rr[2][8];
+                        uint4 rres[2];
+                        bool on[2];
+                        int64_t yo[2];
 #pragma unroll
-                        for (int c = 0; c < 8; ++c) acc8[c] = 0.f;
-                        for (int j = 0; j < fz.k; ++j) {
-                            const int r = fz.row_of[t * fz.k + j];
-                            if (r < 0) continue;
-                            const float g = fz.gw[t * fz.k + j];
-                            float o[8];
-                            const uint64_t *p = (const uint64_t *)(out + (int64_t)r * N + n);
+                        for (int it = 0; it < 2; ++it) {
+                            const int q = q0 + 256 * it;
+                            const int t = q / kC8;
+                            const int n = cb * kCols + (q - t * kC8) * 8;
+                            on[it] = q < n_items && n < N;
+                            const int tq = on[it] ? t : 0, nq = on[it] ? n : 0;
+                            yo[it] = (int64_t)tq * N + nq;
 #pragma unroll
-                            for (int c = 0; c < 4; ++c) {
-                                const uint64_t v = __hip_atomic_load(p + c, __ATOMIC_RELAXED,
-                                                                     __HIP_MEMORY_SCOPE_AGENT);
-                                o[2 * c] = __uint_as_float((uint32_t)v);
-                                o[2 * c + 1] = __uint_as_float((uint32_t)(v >> 32));
+                            for (int j = 0; j < 8; ++j) {
+                                if (j < fz.k) {
+                                    const int a = tq * fz.k + j;
+                                    const int r = s_map[a];
+                                    rr[it][j] = on[it] ? r : -1;
+                                    gv[it][j] = fz.gw[a];
+                                    // written by other workgroups in this launch:
+                                    // agent-coherent loads
+                                    const uint64_t *p =
+                                        (const uint64_t *)(out + (int64_t)max(r, 0) * N + nq);
+#pragma unroll
+                                    for (int c = 0; c < 4; ++c)
+                                        ov[it][j][c] = __hip_atomic_load(
+                                            p + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                }
                             }
-#pragma unroll
-                            for (int c = 0; c < 8; ++c) acc8[c] = fmaf(g, o[c], acc8[c]);
+                            if (fz.residual) rres[it] = *(const uint4 *)(fz.residual + yo[it]);
                         }
-                        if (fz.residual) {
-                            const uint4 rv = *(const uint4 *)(fz.residual + (int64_t)t * N + n);
-                            const uint32_t w4[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                acc8[2 * i] += bf16_bits_to_f32(w4[i] & 0xffffu);
-                                acc8[2 * i + 1] += bf16_bits_to_f32(w4[i] >> 16);
+                        for (int it = 0; it < 2; ++it) {
+                            if (!on[it]) continue;
+                            float acc8[8];
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) acc8[c] = 0.f;
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                if (j < fz.k && rr[it][j] >= 0) {
+#pragma unroll
+                                    for (int c = 0; c < 4; ++c) {
+                                        const uint64_t v = ov[it][j][c];
+                                        acc8[2 * c] = fmaf(gv[it][j], __uint_as_float((uint32_t)v),
+                                                           acc8[2 * c]);
+                                        acc8[2 * c + 1] = fmaf(gv[it][j],
+                                                               __uint_as_float((uint32_t)(v >> 32)),
+                                                               acc8[2 * c + 1]);
+                                    }
+                                }
                             }
+                            if (fz.residual) {
+                                const uint32_t w4[4] = {rres[it].x, rres[it].y, rres[it].z,
+                                                        rres[it].w};
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    acc8[2 * i] += bf16_bits_to_f32(w4[i] & 0xffffu);
+                                    acc8[2 * i + 1] += bf16_bits_to_f32(w4[i] >> 16);
+                                }
+                            }
+                            *(uint4 *)(fz.y + yo[it]) = make_uint4(
+                                pack_bf16x2(acc8[0], acc8[1]), pack_bf16x2(acc8[2], acc8[3]),
+                                pack_bf16x2(acc8[4], acc8[5]), pack_bf16x2(acc8[6], acc8[7]));
                         }
-                        *(uint4 *)(fz.y + (int64_t)t * N + n) =
-                            make_uint4(pack_bf16x2(acc8[0], acc8[1]), pack_bf16x2(acc8[2], acc8[3]),
-                                       pack_bf16x2(acc8[4], acc8[5]), pack_bf16x2(acc8[6], acc8[7]));
                     }
                 }
                 __syncthreads();
