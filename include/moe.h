@@ -88,8 +88,11 @@ const char *moe_expert_ffn_kernels(int64_t T, int d, int d_ff, int E, int k, moe
  * T*k <= 32 (and, on 256 CUs, d_ff <= 16384, d <= 32768 up to four tokens
  * and d <= 16384 for five to eight), the layer runs "stream_cols_kernel"
  * (each workgroup streams its own columns of every active expert over the
- * whole K, GEMM2 forms y); otherwise the same name.  Static storage; "" for
- * shapes the library rejects.  Host only, enqueues nothing. */
+ * whole K, GEMM2 forms y); from 9 to 32 tokens with T*k <= 64 (and d <= 4096
+ * on 256 CUs) it runs GEMM1 on the former and GEMM2 on the latter, named
+ * "stream_gemm_kernel + stream_cols_kernel (W2)"; otherwise the same name.
+ * Static storage; "" for shapes the library rejects.  Host only, enqueues
+ * nothing. */
 const char *moe_forward_kernels(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt);
 
 /* Router: scores, top-k and gates for T tokens.

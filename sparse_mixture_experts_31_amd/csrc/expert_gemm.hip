@@ -406,9 +406,11 @@ const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E
 }
 
 const char *moe_forward_kernel_name(int dt, int64_t T, int k, int d, int d_ff, int E) {
-    if (moe::ffn_path(dt, T * k, d, d_ff, E) == moe::FfnPath::kStream &&
-        moe::stream_cols_supported(T, k, d, d_ff, E))
-        return "stream_cols_kernel";
+    if (moe::ffn_path(dt, T * k, d, d_ff, E) == moe::FfnPath::kStream) {
+        if (moe::stream_cols_supported(T, k, d, d_ff, E)) return "stream_cols_kernel";
+        if (moe::stream_cols_w2_supported(T, k, d, d_ff, E))
+            return "stream_gemm_kernel + stream_cols_kernel (W2)";
+    }
     return moe_expert_ffn_kernel_name(dt, T * k, d, d_ff, E);
 }
 

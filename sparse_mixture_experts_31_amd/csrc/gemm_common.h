@@ -254,6 +254,12 @@ int stream_combine_counters(int d);
 // whole K; GEMM1 writes h and the grouping (fuse.counts, offsets, row_of,
 // token_of), GEMM2 writes y (fuse.gw, residual, y, T, k, topk_idx).
 bool stream_cols_supported(int64_t T, int k, int d, int d_ff, int E);
+// GEMM2 alone on the column kernel for nine to 32 tokens (16 token rows per
+// chunk of an expert's rows), after the tile kernel's GEMM1: hbuf holds h in
+// grouped rows; f.topk_idx, k, gw, residual, y and T as for the above.
+bool stream_cols_w2_supported(int64_t T, int k, int d, int d_ff, int E);
+hipError_t launch_stream_cols_w2(const void *hbuf, const void *W2, int64_t T, int d, int d_ff,
+                                 int E, const StreamFuse &f, hipStream_t s);
 hipError_t launch_stream_cols(const void *x, const void *W1, const void *W3, const void *W2,
                               int64_t T, int d, int d_ff, int E, void *hbuf,
                               const StreamFuse &f, hipEvent_t gemm1_done, hipStream_t s);

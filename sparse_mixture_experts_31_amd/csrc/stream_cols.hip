@@ -38,32 +38,35 @@ namespace moe {
 
 namespace {
 
-constexpr int kCP = 5;         // stages in the ring
-constexpr int kCTB = 5;        // token buffers, one per (expert, K range) in flight
-constexpr int kCAMax = 32;     // assignments T k at most
 constexpr int kCStage = 16 * 1024;
-// A token buffer is reloaded kCTB K ranges (at least kCTB stages) after it
-// was first read, with the load of a stage P - 1 ahead of the consumer: the
-// stages reading it are done by then when kCTB >= P.
-static_assert(kCTB >= kCP, "token buffer reuse");
 
-// Sizes for TOK token rows per expert at most (TOK = 4 for one to four
-// tokens, 8 for five to eight: a token picks an expert once).  Each wave
-// loads TOK / 4 of an expert's token rows with the first stage of its K
-// range and as many dwords into `junk` with the others, so every stage
-// issues LOADS loads per wave.  GEMM2 at TOK = 8 takes at most four column
-// stages per workgroup, to stay within LDS with the larger token buffers.
+// Sizes for TOK token rows per expert (or per chunk of an expert's rows) at
+// most: TOK = 4 for one to four tokens, 8 for five to eight (a token picks an
+// expert once), 16 for GEMM2 alone at nine to 32 tokens, where an expert with
+// more rows is taken in chunks of 16.  Each wave loads TOK / 4 of a chunk's
+// token rows with the first stage of its K range and as many dwords into
+// `junk` with the others, so every stage issues LOADS loads per wave.  The
+// ring has P stages and TB token buffers; a token buffer is reloaded TB K
+// ranges (at least TB stages) after it was first read, with the load of a
+// stage P - 1 ahead of the consumer, so its stages are done when TB >= P.
+// LDS decides the rest: GEMM2 at TOK = 8 takes at most four column stages
+// per workgroup, at TOK = 16 one, with a four-stage ring.
 template <bool SWIGLU, int TOK>
 struct ColsCfg {
+    static constexpr int kP = TOK == 16 ? 4 : 5;
+    static constexpr int kTB = kP;
+    static constexpr int kAMax = TOK == 16 ? 64 : 32;  // assignments T k at most
     static constexpr int kTokLoads = TOK / 4;
     static constexpr int kLoads = 4 + kTokLoads;
     static constexpr int kCPS = SWIGLU ? 8 : 16;  // output columns per stage
-    static constexpr int kMaxS = (SWIGLU || TOK == 4) ? 8 : 4;  // column stages per workgroup
+    static constexpr int kMaxS = (SWIGLU || TOK == 4) ? 8 : TOK == 8 ? 4 : 1;
     static constexpr int kOCols = SWIGLU ? 0 : kMaxS * 16;  // GEMM2 outputs kept per assignment
     static constexpr int kTokBuf = TOK * 1024;
     static constexpr int kRed = kMaxS * 4 * kWave * 16;  // the waves' partial sums of a stage set
-    static constexpr int kLds = kCP * kCStage + kCTB * kTokBuf + 1024 + kCAMax * kOCols * 4 + kRed;
-    static_assert(TOK == 4 || TOK == 8, "token rows per expert");
+    static constexpr int kLds = kP * kCStage + kTB * kTokBuf + 1024 + kAMax * kOCols * 4 + kRed;
+    static_assert(TOK == 4 || TOK == 8 || (TOK == 16 && !SWIGLU), "token rows per chunk");
+    static_assert(kTB >= kP, "token buffer reuse");
+    static_assert(kAMax <= 64, "one lane per assignment");
     static_assert(kLds <= 160 * 1024 - 2 * 1024, "LDS capacity (2 KiB of static tables)");
 };
 
@@ -75,9 +78,8 @@ struct ColsCfg {
 // = h [T k][act_ld], Wa = W2 [E][N][K] (N = d, K = d_ff), y [T][N] receives
 // the combined output.  topk_idx [T k] holds the experts of every (token,
 // slot); out-of-range entries are skipped.  N is a multiple of 512 (16 for
-// the stages), K a multiple of 512, T k <= kCAMax, E <= 64, every expert has
-// at most TOK rows, and the grid leaves each workgroup between 1 and
-// ColsCfg::kMaxS stages of columns.
+// the stages), K a multiple of 512, T k <= ColsCfg::kAMax, E <= 64, and the
+// grid leaves each workgroup between 1 and ColsCfg::kMaxS stages of columns.
 template <bool SWIGLU, int TOK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void stream_cols_kernel(
     const bf16_t *__restrict__ act, int64_t act_ld, const int32_t *__restrict__ topk_idx, int k,
@@ -86,14 +88,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     bf16_t *__restrict__ y, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ row_of, int32_t *__restrict__ token_of) {
     using C = ColsCfg<SWIGLU, TOK>;
-    constexpr int P = kCP, CPS = C::kCPS, MAXS = C::kMaxS, TL = C::kTokLoads;
+    constexpr int P = C::kP, TB = C::kTB, CPS = C::kCPS, MAXS = C::kMaxS, TL = C::kTokLoads;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     char *const ring = smem;
     char *const tbuf = smem + P * kCStage;
-    char *const junk = tbuf + kCTB * C::kTokBuf;
+    char *const junk = tbuf + TB * C::kTokBuf;
     float *const s_o = (float *)(junk + 1024);  // GEMM2: [assignment][column] outputs
-    char *const red = (char *)(s_o + kCAMax * C::kOCols);  // [stage][wave] partial sums
-    __shared__ int s_cnt[64], s_off[64], s_act[64], s_row[kCAMax], s_asg[kCAMax], s_nact;
+    char *const red = (char *)(s_o + C::kAMax * C::kOCols);  // [stage][wave] partial sums
+    // per expert: count, first row; per entry (a chunk of at most TOK of an
+    // expert's rows): expert, first row, rows; per assignment: row; per row:
+    // assignment
+    __shared__ int s_cnt[64], s_off[64], s_ent[64], s_eoff[64], s_ecnt[64];
+    __shared__ int s_row[64], s_asg[64], s_nent;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -123,14 +129,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (lane >= dd) incl += v;
         }
         const int off = incl - cnt;
-        const bool active = lane < E && cnt > 0;
-        const uint64_t am = __ballot(active);
         if (lane < E) {
             s_cnt[lane] = cnt;
             s_off[lane] = off;
         }
-        if (active) s_act[__popcll(am & lower)] = lane;
-        if (lane == 0) s_nact = __popcll(am);
+        // the entries, experts ascending: ceil(cnt / TOK) chunks per expert
+        // (at most 64: each holds a row)
+        const int nch = lane < E ? (cnt + TOK - 1) / TOK : 0;
+        int cincl = nch;
+#pragma unroll
+        for (int dd = 1; dd < kWave; dd <<= 1) {
+            const int v = __shfl_up(cincl, dd);
+            if (lane >= dd) cincl += v;
+        }
+        for (int c = 0; c < nch; ++c) {
+            const int q = cincl - nch + c;
+            s_ent[q] = lane;
+            s_eoff[q] = off + c * TOK;
+            s_ecnt[q] = min(TOK, cnt - c * TOK);
+        }
+        if (lane == kWave - 1) s_nent = cincl;
         const int eoff = __shfl(off, valid ? e : 0);  // every lane takes part
         const int row = valid ? eoff + rank : -1;
         if (lane < A) s_row[lane] = row;
@@ -155,9 +173,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int S = (int)((int64_t)(blockIdx.x + 1) * NU / NG) - u0;
     const int c0 = u0 * CPS;
     const int n_kc = K / 512;
-    const int n_act = u(s_nact);
+    const int n_act = u(s_nent);  // entries
 
-    // Per-expert values, lane i for active expert i (built once, read with
+    // Per-entry values, lane i for entry i (built once, read with
     // readlane, so a stage's addresses never wait on LDS): the byte offset
     // of its weight matrix, of the token rows TL wave + j this wave loads for
     // it (rows past its count repeat its last), its first grouped row and
@@ -167,9 +185,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < TL; ++j) t_tok[j] = 0;
     if (lane < n_act) {
-        const int e = s_act[lane];
-        t_off = s_off[e];
-        t_cnt = s_cnt[e];
+        const int e = s_ent[lane];
+        t_off = s_eoff[lane];
+        t_cnt = s_ecnt[lane];
         t_w = (int64_t)e * N * K * 2;
 #pragma unroll
         for (int j = 0; j < TL; ++j) {
@@ -186,8 +204,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t kb = (int64_t)K * 2;  // bytes per weight row
 
     // ---- producer: P - 1 stages ahead; stage pq goes to slot pq % P.
-    // (pi, pkc, ps): active expert, K range, column stage of the next load;
-    // its token rows go to buffer (pi n_kc + pkc) % kCTB.  Past the last
+    // (pi, pkc, ps): entry, K range, column stage of the next load;
+    // its token rows go to buffer (pi n_kc + pkc) % TB.  Past the last
     // stage the loads are dwords into `junk`, so the counts stay.
     int pi = 0, pkc = 0, ps = 0, pq = 0, pt = 0;
     const char *const dummy = (const char *)act + lane * 4;
@@ -211,7 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 for (int j = 0; j < TL; ++j) {
                     const int jr = TL * wave + j;  // token row in the buffer
                     const char *src = (const char *)act + lane64(t_tok[j], pi) + pkc * 1024;
-                    dma16(src + (lofs ^ (jr << 4)), tbuf + (pt % kCTB) * C::kTokBuf + jr * 1024);
+                    dma16(src + (lofs ^ (jr << 4)), tbuf + (pt % TB) * C::kTokBuf + jr * 1024);
                 }
             } else {
 #pragma unroll
@@ -245,7 +263,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         int cq = 0;  // stages consumed
         for (int i = 0; i < n_act; ++i) {
             for (int kc = 0; kc < n_kc; ++kc) {
-                const char *tb = tbuf + ((i * n_kc + kc) % kCTB) * C::kTokBuf;
+                const char *tb = tbuf + ((i * n_kc + kc) % TB) * C::kTokBuf;
 #pragma unroll
                 for (int s = 0; s < MAXS; ++s) {
                     if (s < S) {
@@ -398,9 +416,29 @@ bool cols_fit(int d, int d_ff) {
 
 bool stream_cols_supported(int64_t T, int k, int d, int d_ff, int E) {
     const int tok = cols_tok(T);
-    if (tok == 0 || T * k > kCAMax || E < 1 || E > 64) return false;
+    if (tok == 0 || T * k > 32 || E < 1 || E > 64) return false;
     if (d < 512 || d_ff < 512 || d % 512 != 0 || d_ff % 512 != 0) return false;
     return tok == 4 ? cols_fit<4>(d, d_ff) : cols_fit<8>(d, d_ff);
+}
+
+bool stream_cols_w2_supported(int64_t T, int k, int d, int d_ff, int E) {
+    using C2 = ColsCfg<false, 16>;
+    if (T < 9 || T > 32 || T * k > C2::kAMax || E < 1 || E > 64) return false;
+    if (d < 512 || d_ff < 512 || d % 512 != 0 || d_ff % 512 != 0) return false;
+    const int s2 = d / C2::kCPS, g2 = cols_grid(s2);
+    return (s2 + g2 - 1) / g2 <= C2::kMaxS;
+}
+
+hipError_t launch_stream_cols_w2(const void *hbuf, const void *W2, int64_t T, int d, int d_ff,
+                                 int E, const StreamFuse &f, hipStream_t s) {
+    using C2 = ColsCfg<false, 16>;
+    hipError_t err = set_lds_limit<stream_cols_kernel<false, 16>>(C2::kLds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((stream_cols_kernel<false, 16>), dim3(cols_grid(d / C2::kCPS)), dim3(256),
+                       C2::kLds, s, (const bf16_t *)hbuf, (int64_t)d_ff, f.topk_idx, f.k, (int)T,
+                       (const bf16_t *)W2, nullptr, E, d, d_ff, nullptr, f.gw, f.residual, f.y,
+                       nullptr, nullptr, nullptr, nullptr);
+    return hipGetLastError();
 }
 
 hipError_t launch_stream_cols(const void *x, const void *W1, const void *W3, const void *W2,

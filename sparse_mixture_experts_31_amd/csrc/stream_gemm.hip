@@ -776,11 +776,13 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
         return launch_stream_cols(x, W1, W3, W2, fuse.T, d, d_ff, E, hbuf, fuse, gemm1_done, s);
     int pieces = stream_layer_pieces(A, d, E);
     if (pieces > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) pieces = 1;
+    // nine to 32 tokens: GEMM2 on the column kernel, which forms y itself
+    const bool w2_cols = fuse.y && stream_cols_w2_supported(fuse.T, fuse.k, d, d_ff, E);
     // GEMM1 reads token rows through the map it builds.  GEMM2 combines in
     // its own tail where its tiles are never split (pieces == 1); else the pass
     // that sums its pieces forms y.
     StreamFuse f1 = fuse;
-    f1.ctr_n = fuse.y && pieces == 1 ? stream_combine_counters(d) : 0;
+    f1.ctr_n = fuse.y && pieces == 1 && !w2_cols ? stream_combine_counters(d) : 0;
     f1.gw = nullptr;
     f1.residual = nullptr;
     f1.y = nullptr;
@@ -788,6 +790,7 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
                                                  d_ff, d, A, hbuf, pieces, partial, s, f1);
     if (err == hipSuccess && gemm1_done) err = hipEventRecord(gemm1_done, s);
     if (err != hipSuccess) return err;
+    if (w2_cols) return launch_stream_cols_w2(hbuf, W2, fuse.T, d, d_ff, E, fuse, s);
     StreamFuse f2{};
     if (pieces == 1 && fuse.y) {
         f2 = fuse;

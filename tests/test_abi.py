@@ -99,7 +99,11 @@ def test_layer_kernel_labels_name_the_column_kernels_up_to_eight_tokens():
                                                                            moe.MOE_BF16)
     for T in range(1, 9):
         assert f(T) == "stream_cols_kernel" and g(T) == "stream_gemm_kernel"
-    assert f(9) == f(99) == "stream_gemm_kernel"
+    hybrid = "stream_gemm_kernel + stream_cols_kernel (W2)"   # GEMM1 tiles, GEMM2 columns
+    assert f(9) == f(32) == hybrid and g(9) == g(32) == "stream_gemm_kernel"
+    assert f(33) == f(99) == "stream_gemm_kernel"
+    assert f(9, d=8192) == "stream_gemm_kernel"          # GEMM2: one column stage at most
+    assert f(16, E=64, k=4) == hybrid and f(17, E=64, k=4) == "stream_gemm_kernel"  # 64 assignments
     assert f(100) == g(100) and f(4096) == g(4096)
     assert f(4, E=64, k=8) == "stream_cols_kernel"       # 32 assignments, the most
     assert f(5, E=64, k=8) == "stream_gemm_kernel"       # 40

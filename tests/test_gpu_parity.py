@@ -383,6 +383,9 @@ def test_expert_parallel_shard_at_the_mixtral_shape(M):
     # decode-sized (T*k/E <= 24): the weight-streaming kernels, here with
     # three token tiles of 32 rows for each of the two experts
     Workload("forced-stream", 21, T=96, d=512, d_ff=1024),
+    # 32 tokens: GEMM2 on the column kernel, each expert's 32 rows in two
+    # chunks of 16 (its W2 rows streamed once per chunk)
+    Workload("forced-chunks", 49, T=32, d=512, d_ff=1024),
 ], ids=lambda w: w.name)
 def test_all_tokens_to_two_experts_and_untouched_experts(w):
     """Every token routes to experts 3 and 5; the other six get no rows, and
@@ -694,6 +697,30 @@ def test_decode_sweep(decode16, T):
     counts = np.bincount(ref["idx"].ravel(), minlength=w.E)
     log(f"  T={T}: {int((counts > 0).sum())} experts active, counts {counts.tolist()}")
     assert (counts > 0).sum() <= min(w.E, 2 * T)
+
+
+@pytest.fixture(scope="module")
+def decode64():
+    """The decode workload's layer at T = 64 (smaller batches take its first
+    T token rows)."""
+    w = WORKLOADS["decode"].with_(name="decode-64", T=64)
+    return w, _case(w)
+
+
+@pytest.mark.parametrize("T", [9, 17, 32, 33, 64])
+def test_decode_batches_around_the_kernel_switches(decode64, T):
+    """Mixtral-shaped batches on both sides of the switches: nine to 32
+    tokens run GEMM1 on the tile kernel and GEMM2 on the column kernel (16
+    token rows per chunk); from 33 on both GEMMs run on the tile kernel,
+    whose GEMM2 forms y in its tail.  Every token must match the oracle."""
+    w0, L0 = decode64
+    w = w0.with_(name=f"decode-T{T}", T=T)
+    L = dict(L0, x=L0["x"][:T].contiguous())
+    want = "stream_gemm_kernel + stream_cols_kernel (W2)" if T <= 32 else "stream_gemm_kernel"
+    assert moe.moe_forward_kernels(T, w.d, w.d_ff, w.E, w.k, torch.bfloat16) == want
+    y, ref = _forward_and_check(w, L)
+    counts = np.bincount(ref["idx"].ravel(), minlength=w.E)
+    log(f"  T={T}: rows per expert {counts.tolist()}")
 
 
 def test_weight_stream_at_every_small_batch():
