@@ -188,12 +188,13 @@ moe_status moe_forward(const void *x, const float *Wg, const void *W1, const voi
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * layer, the same kernels and bit-identical results, with the workspace
  * replaced by a static device array inside the library of
- * moe_forward_noalloc_max_scratch() bytes (32 MiB; each GPU holds its own
- * copy from the first call on it until the process ends).  The caller still
+ * moe_forward_noalloc_max_scratch() bytes (96 MiB of the library's device
+ * data: every GPU the library runs on holds its own copy, from the library's
+ * first use on it until the process ends, whether or not this is called).  The caller still
  * passes x, the weights and y.  Shapes whose workspace,
  * moe_workspace_size(...), exceeds the array return MOE_ERR_WORKSPACE
  * before anything is enqueued (for d = 4096, d_ff = 14336, E = 8, k = 2 the
- * limit is T = 195).  The call allocates and frees nothing.  Every call on a
+ * limit is T = 292).  The call allocates and frees nothing.  Every call on a
  * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
  * other threads) race and must be serialised by the caller. */
 size_t moe_forward_noalloc_max_scratch(void);

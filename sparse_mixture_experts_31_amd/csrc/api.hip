@@ -362,7 +362,7 @@ moe_status moe_forward(const void *x, const float *Wg, const void *W1, const voi
 // and only that address is passed to kernels.  Nothing in it has to start at
 // zero: every kernel of the layer writes what a later kernel of the same call
 // reads.  Calls that overlap on one GPU share the array and race.
-static constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static constexpr size_t kStaticScratchBytes = (size_t)96 << 20;
 static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 namespace {

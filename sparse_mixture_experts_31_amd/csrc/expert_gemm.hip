@@ -299,11 +299,15 @@ enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide };
 // rows (at 32 per expert on average half the experts need two, which
 // streams their weights twice); the large tiles win from about 56 rows per
 // expert on, since smaller tiles re-read the weights for every token tile.
+// (Those wide figures are 256-row token tiles; with 128-row tiles, used up to
+// 100 rows per expert, the wide kernels also beat the grouped ones at 25-48
+// rows per expert, 561-575 against 611-659 us at T = 100-195, so bf16 takes
+// them from 25 rows per expert on.)
 static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
     const int64_t per_expert = A / E;
     const bool stream = dt == 1 && stream_supported(A, d, d_ff, E);
     if (stream && per_expert <= 24) return FfnPath::kStream;
-    if (dt == 1 && per_expert > 48 && wide_supported(A, d, d_ff)) return FfnPath::kWide;
+    if (dt == 1 && per_expert > 24 && wide_supported(A, d, d_ff)) return FfnPath::kWide;
     if (per_expert <= 32 && !stream) return FfnPath::kSkinny;
     if (per_expert <= 256) return FfnPath::kGroupedSmall;
     return FfnPath::kGroupedLarge;
@@ -417,7 +421,7 @@ const char *moe_forward_kernel_name(int dt, int64_t T, int k, int d, int d_ff, i
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E) {
     switch (moe::ffn_path(dt, A, d, d_ff, E)) {
         case moe::FfnPath::kWide:
-            return moe::wide_partial_bytes();
+            return moe::wide_partial_bytes(A, E);
         case moe::FfnPath::kStream:
             return moe::stream_partial_bytes(A, d, d_ff, E);
         default:

@@ -270,7 +270,7 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
 
 // Wide-tile expert GEMMs (wide_gemm.hip), bf16 only.  `partial` (may be
 // NULL) is scratch for split tiles, at least wide_partial_bytes() bytes.
-size_t wide_partial_bytes();
+size_t wide_partial_bytes(int64_t A, int E);
 // Token-tile height (128 or 256) the wide kernels use for A rows over E experts.
 int wide_token_tile(int64_t A, int E);
 bool wide_supported(int64_t A, int d, int d_ff);

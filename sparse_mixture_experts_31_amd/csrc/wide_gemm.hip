@@ -60,13 +60,13 @@ struct WideTile {
     static constexpr int kLds = kWideP * kStageBytes + kWidePfBytes;
     static constexpr int kNJ = BT / 32;  // token fragments per wave
     static constexpr int kFW = 8 * kNJ;  // fragments per wave
+    // a scratch slot: the accumulators of one workgroup
+    static constexpr int kSlotFloats = kWideWaves * kWave * 4 * kFW;
     static_assert(kLPW * (kWideP - 1) < 64, "vmcnt range");
     static_assert(kLds <= 160 * 1024 - 1024, "LDS capacity");
 };
 constexpr int kWidePfAhead = 2;   // stages past the one being loaded
 constexpr int kWideKStep = 64;                   // bf16 K elements per stage
-// A scratch slot: the accumulators of one workgroup of 256-row tiles.
-constexpr int kSlotFloats = kWideWaves * kWave * 4 * WideTile<256>::kFW;
 
 // Byte offset of 16-byte chunk c of row r in a stage of 128-byte rows: the
 // chunk sits at c ^ ((r >> 1) & 7), so a 32-row operand read (16 lanes per
@@ -167,8 +167,9 @@ __device__ __forceinline__ void pin_accumulators(f32x4 (&acc)[8][NJ]) {
 
 // Scratch slot layout: fragment p = NJ i + j of thread t at float4
 // p * 256 + t, so every store and load of a wave is 1 KiB contiguous.
+template <int BT>
 __device__ __forceinline__ float *slot_ptr(float *partial, int slot) {
-    return partial + (size_t)slot * kSlotFloats;
+    return partial + (size_t)slot * WideTile<BT>::kSlotFloats;
 }
 
 }  // namespace
@@ -438,7 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             }
         } else {
-            float *dst = slot_ptr(partial, blockIdx.x * 2 + cur.slot);
+            float *dst = slot_ptr<BT>(partial, blockIdx.x * 2 + cur.slot);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -508,7 +509,8 @@ __global__ __launch_bounds__(256) void wide_fixup_kernel(const int32_t *__restri
         f32x4 r{};
 #pragma unroll 4
         for (int k = 0; k < np; ++k)
-            r += *(const f32x4 *)(partial + (size_t)s_slots[k] * kSlotFloats + 4 * (p * 256 + tid));
+            r += *(const f32x4 *)(partial + (size_t)s_slots[k] * WideTile<BT>::kSlotFloats +
+                                  4 * (p * 256 + tid));
         return r;
     };
 #pragma unroll
@@ -562,7 +564,11 @@ hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, c
 
 int wide_token_tile(int64_t A, int E) { return A <= 100 * (int64_t)E ? 128 : 256; }
 
-size_t wide_partial_bytes() { return (size_t)2 * wide_grid() * kSlotFloats * sizeof(float); }
+size_t wide_partial_bytes(int64_t A, int E) {
+    const size_t slot = wide_token_tile(A, E) == 128 ? WideTile<128>::kSlotFloats
+                                                     : WideTile<256>::kSlotFloats;
+    return (size_t)2 * wide_grid() * slot * sizeof(float);
+}
 
 bool wide_supported(int64_t A, int d, int d_ff) {
     // load addresses are 32-bit offsets from a tile's bases: token rows are
@@ -576,7 +582,7 @@ hipError_t launch_wide_ffn(const void *act, const int32_t *gather, const int32_t
                            const void *W1, const void *W3, const void *W2, int out_f32, int64_t A,
                            int d, int d_ff, int E, void *hbuf, void *out, float *partial,
                            size_t partial_bytes, hipEvent_t mid, hipStream_t s) {
-    if (partial && partial_bytes < wide_partial_bytes()) partial = nullptr;  // no splits
+    if (partial && partial_bytes < wide_partial_bytes(A, E)) partial = nullptr;  // no splits
     hipError_t err = launch_wide<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A,
                                                hbuf, partial, s);
     if (err == hipSuccess && mid) err = hipEventRecord(mid, s);

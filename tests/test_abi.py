@@ -72,13 +72,15 @@ def test_permute_workspace_size_rules():
 
 def test_kernel_family_labels_follow_rows_per_expert():
     """The expert kernels are chosen by rows per expert (T k / E) on the host:
-    the weight stream below 25, the 128 x 64 grouped kernels below 49, the
-    wide kernels above (128-row token tiles up to 100, then 256), bf16 only
-    for the stream and wide kernels."""
-    f = lambda T, E=8, k=2, dt=moe.MOE_BF16: moe.moe_expert_ffn_kernels(T, 4096, 14336, E, k, dt)
+    the weight stream below 25, the wide kernels above (128-row token tiles
+    up to 100, then 256), bf16 only for the stream and wide kernels; the
+    grouped kernels take the rest (fp32, and d or d_ff too small for the
+    wide tiles)."""
+    f = lambda T, E=8, k=2, dt=moe.MOE_BF16, d=4096: moe.moe_expert_ffn_kernels(
+        T, d, 14336, E, k, dt)
     assert f(1) == f(99) == "stream_gemm_kernel"
-    assert f(100).startswith("grouped_gemm_kernel (128 x 64")
-    assert f(195).startswith("grouped_gemm_kernel (128 x 64")
+    assert f(100) == f(195) == "wide_gemm_kernel (128-row token tiles)"
+    assert f(160, d=64).startswith("grouped_gemm_kernel (128 x 64")  # too small for wide
     assert f(196) == "wide_gemm_kernel (128-row token tiles)"
     assert f(400) == "wide_gemm_kernel (128-row token tiles)"
     assert f(401) == f(4096) == "wide_gemm_kernel (256-row token tiles)"
@@ -212,16 +214,16 @@ def test_noalloc_entry_point_rejects_shapes_beyond_its_array():
     happens (no device is touched), smaller ones pass this check."""
     L = moe.lib()
     cap = L.moe_forward_noalloc_max_scratch()
-    assert cap == 32 << 20
+    assert cap == 96 << 20
     ws = moe.moe_workspace_size
-    assert ws(195, 4096, 14336, 8, 2, moe.MOE_BF16) <= cap < ws(196, 4096, 14336, 8, 2,
+    assert ws(292, 4096, 14336, 8, 2, moe.MOE_BF16) <= cap < ws(293, 4096, 14336, 8, 2,
                                                                moe.MOE_BF16)
 
     def call(T):
         return L.moe_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, moe.MOE_BF16, T, 4096, 14336,
                                      8, 2, FAKE, None)
 
-    assert call(196) == moe.MOE_ERR_WORKSPACE
+    assert call(293) == moe.MOE_ERR_WORKSPACE
     assert "static array" in L.moe_last_error().decode()
     assert call(-1) == moe.MOE_ERR_INVALID_ARG
     assert call(0) == moe.MOE_OK

@@ -66,8 +66,12 @@ SMALL = [
     # workgroups (the ring crosses tile boundaries), 2 K ranges of 512 in
     # GEMM1 and 10 in GEMM2
     Workload("stream-tiles", 23, T=24, d=1024, d_ff=5120),
-    # 25-48 rows per expert: the grouped kernels with 128 x 64 tiles (bf16)
-    Workload("grouped-bf16", 26, T=160, d=512, d_ff=1024),
+    # 40 rows per expert with d too small for the wide tiles: the grouped
+    # kernels with 128 x 64 tiles (bf16)
+    Workload("grouped-bf16", 26, T=160, d=64, d_ff=1024),
+    # 25-48 rows per expert: the wide kernels with 128-row token tiles and
+    # their split last round
+    Workload("wide-mid", 50, T=160, d=512, d_ff=1024),
     # degenerate routing: one expert (every gate is 1), and every token
     # taking all eight experts
     Workload("e1-k1", 27, T=50, d=256, d_ff=512, E=1, k=1),
@@ -656,9 +660,8 @@ def prefill_layer():
 
 @pytest.mark.parametrize("T,family", [
     (99, "stream_gemm_kernel"),                      # 24 rows per expert on average
-    (100, "grouped_gemm_kernel (128 x 64 tiles)"),   # 25
-    (195, "grouped_gemm_kernel (128 x 64 tiles)"),   # 48
-    (196, "wide_gemm_kernel (128-row token tiles)"),  # 49
+    (100, "wide_gemm_kernel (128-row token tiles)"),  # 25
+    (160, "wide_gemm_kernel (128-row token tiles)"),  # 40
     (400, "wide_gemm_kernel (128-row token tiles)"),  # 100
     (401, "wide_gemm_kernel (256-row token tiles)"),  # 100.25
 ])

@@ -19,8 +19,10 @@ DEV = "cuda"
 @pytest.mark.parametrize("w", [
     # the decode workload: T = 32 (whole tiles), then 8 (the column kernels)
     WORKLOADS["decode"],
-    # mid-sized grouped tiles and fp32
-    Workload("noalloc-grouped", 50, T=150, d=512, d_ff=1024),
+    # mid-sized: the wide kernels with their split scratch, grouped tiles
+    # (d too small for the wide ones), and fp32
+    Workload("noalloc-wide", 50, T=150, d=512, d_ff=1024),
+    Workload("noalloc-grouped", 53, T=150, d=64, d_ff=1024),
     Workload("noalloc-f32", 51, T=64, d=256, d_ff=448, dtype="f32"),
     # four tokens, then one: the column kernels
     Workload("noalloc-few-tokens", 52, T=4, d=1024, d_ff=2048),
@@ -48,7 +50,7 @@ def test_noalloc_forward_matches_moe_forward(w):
 
 def test_noalloc_refuses_shapes_beyond_the_array():
     w = WORKLOADS["decode"]
-    x = torch.zeros((196, w.d), dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros((293, w.d), dtype=torch.bfloat16, device=DEV)
     Wg = torch.zeros((w.E, w.d), dtype=torch.float32, device=DEV)
     W = torch.zeros((w.E, 64, w.d), dtype=torch.bfloat16, device=DEV)   # never read
     W2 = torch.zeros((w.E, w.d, 64), dtype=torch.bfloat16, device=DEV)
