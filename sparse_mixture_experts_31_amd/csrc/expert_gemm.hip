@@ -287,7 +287,7 @@ static hipError_t launch_grouped(const void *act, int64_t act_ld, const void *Wa
 // (stream_gemm.hip for bf16, skinny_gemm.hip for fp32 or small d), mid-sized
 // ones use 8-wave grouped tiles, large bf16 ones the wide tiles
 // (wide_gemm.hip).
-enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide };
+enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide, kMixed };
 
 // Which kernels run the experts, by the average rows per expert (measured on
 // MI355X at d = 4096, d_ff = 14336, E = 8, k = 2; layer times in us):
@@ -299,15 +299,18 @@ enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide };
 // rows (at 32 per expert on average half the experts need two, which
 // streams their weights twice); the large tiles win from about 56 rows per
 // expert on, since smaller tiles re-read the weights for every token tile.
-// (Those wide figures are 256-row token tiles; with 128-row tiles, used up to
-// 100 rows per expert, the wide kernels also beat the grouped ones at 25-48
-// rows per expert, 561-575 against 611-659 us at T = 100-195, so bf16 takes
-// them from 25 rows per expert on.)
+// (Those wide figures are 256-row token tiles.  At 25-48 rows per expert the
+// wide kernels' GEMM2 with 128-row token tiles beats the grouped one by a
+// quarter, 181-186 against 251-264 us at T = 100-195, while their GEMM1,
+// whose 128-row tiles are mostly padding there, loses to the grouped 64-row
+// tiles, 367-378 against 335-358 us: bf16 takes the grouped GEMM1 and the
+// wide GEMM2 there, the wide kernels for both from 49 on.)
 static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
     const int64_t per_expert = A / E;
     const bool stream = dt == 1 && stream_supported(A, d, d_ff, E);
     if (stream && per_expert <= 24) return FfnPath::kStream;
-    if (dt == 1 && per_expert > 24 && wide_supported(A, d, d_ff)) return FfnPath::kWide;
+    if (dt == 1 && per_expert > 24 && wide_supported(A, d, d_ff))
+        return per_expert <= 48 ? FfnPath::kMixed : FfnPath::kWide;
     if (per_expert <= 32 && !stream) return FfnPath::kSkinny;
     if (per_expert <= 256) return FfnPath::kGroupedSmall;
     return FfnPath::kGroupedLarge;
@@ -345,6 +348,13 @@ static hipError_t launch_ffn_typed(const void *act, const int32_t *gather,
             return launch_wide_ffn(act, gather, offsets, W1, W3, W2, ElemSize<TO>::value == 4, A,
                                    d, d_ff, E, hbuf, out, (float *)scratch, scratch_bytes, mid,
                                    s);
+        case FfnPath::kMixed:
+            err = launch_grouped<128, 64, 2, 2, 6, true, T>(act, d, W1, W3, offsets, E, d_ff, d,
+                                                             A, hbuf, 2, s);
+            if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
+            if (err != hipSuccess) return err;
+            return launch_wide_w2(hbuf, offsets, W2, ElemSize<TO>::value == 4, A, d, d_ff, E, out,
+                                  (float *)scratch, scratch_bytes, s);
         case FfnPath::kGroupedLarge:
             break;
     }
@@ -405,6 +415,9 @@ const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E
         case moe::FfnPath::kWide:
             return moe::wide_token_tile(A, E) == 128 ? "wide_gemm_kernel (128-row token tiles)"
                                                      : "wide_gemm_kernel (256-row token tiles)";
+        case moe::FfnPath::kMixed:
+            return "grouped_gemm_kernel (128 x 64 tiles) + wide_gemm_kernel (128-row token tiles) "
+                   "(W2)";
     }
     return "";
 }
@@ -421,6 +434,7 @@ const char *moe_forward_kernel_name(int dt, int64_t T, int k, int d, int d_ff, i
 size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E) {
     switch (moe::ffn_path(dt, A, d, d_ff, E)) {
         case moe::FfnPath::kWide:
+        case moe::FfnPath::kMixed:
             return moe::wide_partial_bytes(A, E);
         case moe::FfnPath::kStream:
             return moe::stream_partial_bytes(A, d, d_ff, E);

@@ -271,6 +271,11 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
 // Wide-tile expert GEMMs (wide_gemm.hip), bf16 only.  `partial` (may be
 // NULL) is scratch for split tiles, at least wide_partial_bytes() bytes.
 size_t wide_partial_bytes(int64_t A, int E);
+// GEMM2 alone on the wide kernels (h in expert order, rows [offsets[0],
+// offsets[E]) ), for the mixed path: grouped GEMM1, wide GEMM2.
+hipError_t launch_wide_w2(const void *hbuf, const int32_t *offsets, const void *W2, int out_f32,
+                          int64_t A, int d, int d_ff, int E, void *out, float *partial,
+                          size_t partial_bytes, hipStream_t s);
 // Token-tile height (128 or 256) the wide kernels use for A rows over E experts.
 int wide_token_tile(int64_t A, int E);
 bool wide_supported(int64_t A, int d, int d_ff);

@@ -594,4 +594,15 @@ hipError_t launch_wide_ffn(const void *act, const int32_t *gather, const int32_t
                                       out, partial, s);
 }
 
+hipError_t launch_wide_w2(const void *hbuf, const int32_t *offsets, const void *W2, int out_f32,
+                          int64_t A, int d, int d_ff, int E, void *out, float *partial,
+                          size_t partial_bytes, hipStream_t s) {
+    if (partial && partial_bytes < wide_partial_bytes(A, E)) partial = nullptr;  // no splits
+    if (out_f32)
+        return launch_wide<false, float>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff,
+                                         A, out, partial, s);
+    return launch_wide<false, bf16_t>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff, A,
+                                      out, partial, s);
+}
+
 }  // namespace moe

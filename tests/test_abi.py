@@ -72,14 +72,16 @@ def test_permute_workspace_size_rules():
 
 def test_kernel_family_labels_follow_rows_per_expert():
     """The expert kernels are chosen by rows per expert (T k / E) on the host:
-    the weight stream below 25, the wide kernels above (128-row token tiles
-    up to 100, then 256), bf16 only for the stream and wide kernels; the
-    grouped kernels take the rest (fp32, and d or d_ff too small for the
-    wide tiles)."""
+    the weight stream below 25, grouped GEMM1 with wide GEMM2 below 49, the
+    wide kernels above (128-row token tiles up to 100, then 256), bf16 only
+    for the stream and wide kernels; the grouped kernels take the rest
+    (fp32, and d or d_ff too small for the wide tiles)."""
     f = lambda T, E=8, k=2, dt=moe.MOE_BF16, d=4096: moe.moe_expert_ffn_kernels(
         T, d, 14336, E, k, dt)
     assert f(1) == f(99) == "stream_gemm_kernel"
-    assert f(100) == f(195) == "wide_gemm_kernel (128-row token tiles)"
+    assert f(100) == f(195) == ("grouped_gemm_kernel (128 x 64 tiles) + "
+                                "wide_gemm_kernel (128-row token tiles) (W2)")
+    assert f(196) == "wide_gemm_kernel (128-row token tiles)"
     assert f(160, d=64).startswith("grouped_gemm_kernel (128 x 64")  # too small for wide
     assert f(196) == "wide_gemm_kernel (128-row token tiles)"
     assert f(400) == "wide_gemm_kernel (128-row token tiles)"

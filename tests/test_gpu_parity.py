@@ -69,9 +69,9 @@ SMALL = [
     # 40 rows per expert with d too small for the wide tiles: the grouped
     # kernels with 128 x 64 tiles (bf16)
     Workload("grouped-bf16", 26, T=160, d=64, d_ff=1024),
-    # 25-48 rows per expert: the wide kernels with 128-row token tiles and
-    # their split last round
-    Workload("wide-mid", 50, T=160, d=512, d_ff=1024),
+    # 25-48 rows per expert: grouped GEMM1, then GEMM2 on the wide kernels
+    # with 128-row token tiles and their split last round
+    Workload("mixed-mid", 50, T=160, d=512, d_ff=1024),
     # degenerate routing: one expert (every gate is 1), and every token
     # taking all eight experts
     Workload("e1-k1", 27, T=50, d=256, d_ff=512, E=1, k=1),
@@ -658,10 +658,14 @@ def prefill_layer():
     return w, _case(w)
 
 
+MIXED = "grouped_gemm_kernel (128 x 64 tiles) + wide_gemm_kernel (128-row token tiles) (W2)"
+
+
 @pytest.mark.parametrize("T,family", [
     (99, "stream_gemm_kernel"),                      # 24 rows per expert on average
-    (100, "wide_gemm_kernel (128-row token tiles)"),  # 25
-    (160, "wide_gemm_kernel (128-row token tiles)"),  # 40
+    (100, MIXED),                                    # 25
+    (195, MIXED),                                    # 48
+    (196, "wide_gemm_kernel (128-row token tiles)"),  # 49
     (400, "wide_gemm_kernel (128-row token tiles)"),  # 100
     (401, "wide_gemm_kernel (256-row token tiles)"),  # 100.25
 ])

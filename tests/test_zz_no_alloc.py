@@ -19,9 +19,9 @@ DEV = "cuda"
 @pytest.mark.parametrize("w", [
     # the decode workload: T = 32 (whole tiles), then 8 (the column kernels)
     WORKLOADS["decode"],
-    # mid-sized: the wide kernels with their split scratch, grouped tiles
-    # (d too small for the wide ones), and fp32
-    Workload("noalloc-wide", 50, T=150, d=512, d_ff=1024),
+    # mid-sized: grouped GEMM1 and the wide GEMM2 with its split scratch,
+    # grouped tiles alone (d too small for the wide ones), and fp32
+    Workload("noalloc-mixed", 50, T=150, d=512, d_ff=1024),
     Workload("noalloc-grouped", 53, T=150, d=64, d_ff=1024),
     Workload("noalloc-f32", 51, T=64, d=256, d_ff=448, dtype="f32"),
     # four tokens, then one: the column kernels
