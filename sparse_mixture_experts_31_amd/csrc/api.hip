@@ -76,7 +76,7 @@ size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace segments of the fused calls, in order.
 struct Carve {
-    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, split, ctr, dsc,
+    size_t idx, gw, counts, offsets, row_of, token_of, x_perm, o_perm, h, xn, split, dsc,
         total;
     size_t split_bytes;
 };
@@ -97,7 +97,6 @@ Carve carve(int64_t T, int d, int d_ff, int E, int k, moe_dtype dt) {
     c.xn = o;       o += up((size_t)T * d * es);
     c.split_bytes = moe_expert_ffn_scratch_bytes((int)dt, (int64_t)A, d, d_ff, E);
     c.split = o;    o += up(c.split_bytes);  // partial sums of K-split expert tiles
-    c.ctr = o;      o += up((size_t)moe_stream_combine_counters(d) * 4);  // decode combine
     c.dsc = o;      o += up(moe_dispatch_scratch_bytes((int64_t)A, E));  // dispatch chunk counts
     c.total = o;
     return c;
@@ -296,10 +295,11 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
     LAUNCH(mark(1), "event");
     if (moe_expert_ffn_streams((int)dt, A, d, d_ff, E)) {
         // Decode sizes: the weight-streaming GEMM1 groups the assignments
-        // itself and GEMM2 also combines (dispatch and combine stages empty).
+        // itself, and GEMM2 or the pass after it also combines (dispatch and
+        // combine stages empty).
         LAUNCH(mark(2), "event");
         LAUNCH(moe_launch_stream_layer(x, idx, k, gw, residual, W1, W3, W2, T, d, d_ff, E, counts,
-                                       offsets, row_of, token_of, at<int32_t>(ws, c.ctr), hbuf,
+                                       offsets, row_of, token_of, hbuf,
                                        (float *)o_perm, y,
                                        c.split_bytes ? at<char>(ws, c.split) : nullptr,
                                        c.split_bytes, ev ? (hipEvent_t)ev[3] : nullptr, s),

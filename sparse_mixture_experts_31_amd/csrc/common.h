@@ -96,18 +96,17 @@ size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E);
 // The decode layer's experts on the weight-streaming kernels
 // (moe_expert_ffn_streams()): GEMM1 groups the assignments itself (topk_idx,
 // k slots per token; counts, offsets, row_of, token_of written out), and
-// GEMM2 (or, where its tiles may be split, the pass that sums their pieces)
-// also writes y = sum_j gw o_j (+ residual) (bf16; o_perm fp32 in between;
-// ctr: moe_stream_combine_counters(d) ints of scratch).
+// GEMM2, or the pass after it, also writes y = sum_j gw o_j (+ residual)
+// (bf16; o_perm fp32 in between).  scratch: at least
+// moe_expert_ffn_scratch_bytes() of the shape (the split-tile scratch).
 bool moe_expert_ffn_streams(int dt, int64_t A, int d, int d_ff, int E);
-int moe_stream_combine_counters(int d);
 hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k, const float *gw,
                                    const void *residual, const void *W1, const void *W3,
                                    const void *W2, int64_t T, int d, int d_ff, int E,
                                    int32_t *counts, int32_t *offsets, int32_t *row_of,
-                                   int32_t *token_of, int32_t *ctr, void *hbuf, float *o_perm,
-                                   void *y, void *scratch, size_t scratch_bytes,
-                                   hipEvent_t gemm1_done, hipStream_t s);
+                                   int32_t *token_of, void *hbuf, float *o_perm, void *y,
+                                   void *scratch, size_t scratch_bytes, hipEvent_t gemm1_done,
+                                   hipStream_t s);
 // Name of the kernel family that runs the experts for this shape.
 const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E);
 // The same for the experts of the fused layer (moe_forward and friends) at T

@@ -295,9 +295,11 @@ enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide, kMix
 //   stream   459   815  1145  1300  2056  3676
 //   grouped  605   615   632   867  1254  1892
 //   wide     653   659   669   690   722   954
-// The weight stream wins while one 32-row token tile holds every expert's
-// rows (at 32 per expert on average half the experts need two, which
-// streams their weights twice); the large tiles win from about 56 rows per
+// The weight stream wins while one 32-row token tile holds nearly every
+// expert's rows (an expert with more streams its weights twice; with the even
+// K split balancing the tiles, the stream ran the layer in 0.443 ms at 26
+// rows per expert on average, 0.549 at 27 against 0.550 for the kernels
+// below, and lost from 29 on); the large tiles win from about 56 rows per
 // expert on, since smaller tiles re-read the weights for every token tile.
 // (Those wide figures are 256-row token tiles.  At 25-48 rows per expert the
 // wide kernels' GEMM2 with 128-row token tiles beats the grouped one by a
@@ -308,7 +310,7 @@ enum class FfnPath { kStream, kSkinny, kGroupedSmall, kGroupedLarge, kWide, kMix
 static FfnPath ffn_path(int dt, int64_t A, int d, int d_ff, int E) {
     const int64_t per_expert = A / E;
     const bool stream = dt == 1 && stream_supported(A, d, d_ff, E);
-    if (stream && per_expert <= 24) return FfnPath::kStream;
+    if (stream && per_expert <= 26) return FfnPath::kStream;
     if (dt == 1 && per_expert > 24 && wide_supported(A, d, d_ff))
         return per_expert <= 48 ? FfnPath::kMixed : FfnPath::kWide;
     if (per_expert <= 32 && !stream) return FfnPath::kSkinny;
@@ -376,15 +378,14 @@ bool moe_expert_ffn_streams(int dt, int64_t A, int d, int d_ff, int E) {
     return moe::ffn_path(dt, A, d, d_ff, E) == moe::FfnPath::kStream;
 }
 
-int moe_stream_combine_counters(int d) { return moe::stream_combine_counters(d); }
 
 hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k, const float *gw,
                                    const void *residual, const void *W1, const void *W3,
                                    const void *W2, int64_t T, int d, int d_ff, int E,
                                    int32_t *counts, int32_t *offsets, int32_t *row_of,
-                                   int32_t *token_of, int32_t *ctr, void *hbuf, float *o_perm,
-                                   void *y, void *scratch, size_t scratch_bytes,
-                                   hipEvent_t gemm1_done, hipStream_t s) {
+                                   int32_t *token_of, void *hbuf, float *o_perm, void *y,
+                                   void *scratch, size_t scratch_bytes, hipEvent_t gemm1_done,
+                                   hipStream_t s) {
     const int64_t A = T * k;
     moe::StreamFuse f{};
     f.topk_idx = topk_idx;
@@ -393,7 +394,6 @@ hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k
     f.offsets = offsets;
     f.row_of = row_of;
     f.token_of = token_of;
-    f.ctr = ctr;
     f.gw = gw;
     f.residual = (const moe::bf16_t *)residual;
     f.y = (moe::bf16_t *)y;

@@ -212,22 +212,19 @@ static inline int device_cus() {
 }
 
 // What the decode path folds into the weight-streaming kernels
-// (stream_gemm.hip), so a layer is three launches: router, GEMM1, GEMM2.
-// All NULL / 0: the kernels run alone.
+// (stream_gemm.hip, stream_cols.hip): no dispatch launch before GEMM1 and
+// no separate combine launch.  All NULL / 0: the kernels run alone.
 struct StreamFuse {
-    // GEMM1 groups the assignments itself (no dispatch launch): topk_idx
-    // [A] holds the expert of every (token, slot), k slots per token; every
-    // workgroup derives the same stable grouping, workgroup 0 writes it out
-    // (counts [E], offsets [E+1], row_of [A], token_of [A]) and zeroes
-    // GEMM2's ctr_n combine counters.
+    // GEMM1 groups the assignments itself: topk_idx [A] holds the expert of
+    // every (token, slot), k slots per token; every workgroup derives the
+    // same stable grouping, workgroup 0 writes it out (counts [E], offsets
+    // [E+1], row_of [A], token_of [A]).
     const int32_t *topk_idx;
     int k;
     int32_t *counts, *offsets, *row_of, *token_of;
-    int32_t *ctr;
-    int ctr_n;
-    // GEMM2 (fp32 expert outputs) combines: the last workgroup to finish a
-    // column block writes y[t] = sum_j gw[t][j] out[row_of[t][j]] (+
-    // residual[t]) for every token t < T on that block's columns.
+    // y[t] = sum_j gw[t][j] o[row_of[t][j]] (+ residual[t]) for the T tokens,
+    // formed by the column kernels' GEMM2 or by the pass after the tile
+    // kernels' GEMM2.
     const float *gw;
     const bf16_t *residual;
     bf16_t *y;
@@ -246,9 +243,13 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
                              float *partial, size_t partial_bytes, hipEvent_t mid,
                              hipStream_t s);
 // The decode layer's experts with the grouping folded into GEMM1 and the
-// combine into GEMM2 or the pass after it (out: fp32 expert outputs).  act
-// is x (rows read in place); offsets receives the grouping (fuse.offsets).
-int stream_combine_counters(int d);
+// combine into GEMM2 or the pass after it (out: fp32 expert outputs; x rows
+// read in place; fuse.offsets receives the grouping).  The tile kernels need
+// the split scratch (partial, stream_partial_bytes()) here.
+hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, const void *W2,
+                               int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
+                               float *partial, size_t partial_bytes, const StreamFuse &fuse,
+                               hipEvent_t gemm1_done, hipStream_t s);
 // The decode layer's experts for one to eight tokens (stream_cols.hip):
 // every workgroup streams its own columns of every active expert over the
 // whole K; GEMM1 writes h and the grouping (fuse.counts, offsets, row_of,
@@ -263,10 +264,6 @@ hipError_t launch_stream_cols_w2(const void *hbuf, const void *W2, int64_t T, in
 hipError_t launch_stream_cols(const void *x, const void *W1, const void *W3, const void *W2,
                               int64_t T, int d, int d_ff, int E, void *hbuf,
                               const StreamFuse &f, hipEvent_t gemm1_done, hipStream_t s);
-hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, const void *W2,
-                               int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
-                               float *partial, size_t partial_bytes, const StreamFuse &fuse,
-                               hipEvent_t gemm1_done, hipStream_t s);
 
 // Wide-tile expert GEMMs (wide_gemm.hip), bf16 only.  `partial` (may be
 // NULL) is scratch for split tiles, at least wide_partial_bytes() bytes.

@@ -125,8 +125,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (writer) f.offsets[E_] = incl;
             }
         }
-        if (writer && f.ctr)
-            for (int i = t; i < f.ctr_n; i += 256) f.ctr[i] = 0;
         __syncthreads();
         const uint64_t lower = (ln == 0) ? 0ull : (~0ull >> (64 - ln));
         for (int r0 = 0; r0 < A_; r0 += 256) {
@@ -175,10 +173,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (wave == 0) build_expert_table(s_goff, E, A, kSBT, col_tiles, s_lo, s_cnt, s_first);
     } else if (wave == 0) {
         build_expert_table(offsets, E, A, kSBT, col_tiles, s_lo, s_cnt, s_first);
-    } else if (gather || (!SWIGLU && fz.y)) {
-        // the token map; or, for GEMM2 forming y (no map to read), row_of,
-        // which the combine in its tail looks up for every (token, slot)
-        const int32_t *src = gather ? gather : fz.row_of;
+    } else if (gather) {
+        const int32_t *src = gather;
         constexpr int kStride = 256 - kWave;
         for (int i0 = tid - kWave; i0 < A; i0 += 4 * kStride) {
             int v[4];
@@ -472,19 +468,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                             r[q] = acc[h][q];
                             if constexpr (SWIGLU) r[q] = silu(r[q]) * acc[h + 2][q];
                         }
-                        if (!SWIGLU && fz.y) {
-                            // read by another workgroup in this launch: written
-                            // through to memory (agent-coherent stores)
-                            uint64_t *p = (uint64_t *)(out + row * N + n);
-                            __hip_atomic_store(p, ((uint64_t)__float_as_uint(r[1]) << 32) |
-                                                      __float_as_uint(r[0]),
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            __hip_atomic_store(p + 1, ((uint64_t)__float_as_uint(r[3]) << 32) |
-                                                          __float_as_uint(r[2]),
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        } else {
-                            store4<TO>(out + row * N + n, r[0], r[1], r[2], r[3]);
-                        }
+                        store4<TO>(out + row * N + n, r[0], r[1], r[2], r[3]);
                     }
                 }
             }
@@ -493,105 +477,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = 0; i < 4; ++i) acc[i] = f32x4{};
     }
     wait_vmcnt_lgkm0<0>();  // the trailing reloads land before the wave ends
-
-    // The decode layer's combine (GEMM2, fp32 outputs, whole tiles): this
-    // workgroup's tiles are counted in their column blocks; the workgroup
-    // that completes a block (every token tile of every expert on its
-    // columns stored) forms y on those columns for all T tokens.  The
-    // outputs were written through to memory and every wave waited for its
-    // stores (above) before the count, and the completing workgroup reads
-    // them with agent-coherent loads: no cache flush or invalidation (those
-    // stall the other workgroups of the XCD still streaming).
-    if constexpr (!SWIGLU && std::is_same<TO, float>::value) {
-        if (fz.y && !split) {
-            __shared__ int s_done;
-            __syncthreads();
-            const int per_block = tiles / col_tiles;  // token tiles of all experts
-            for (int ck = 0; ck < my_items; ++ck) {
-                const int cb = item_info(ck).ti.n0 / kCols;
-                if (tid == 0)
-                    s_done = __hip_atomic_fetch_add(&fz.ctr[cb], 1, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT) == per_block - 1;
-                __syncthreads();
-                if (s_done) {
-                    // Two 8-column pieces per thread and pass, every load of
-                    // both issued before either is summed (row_of from LDS):
-                    // one memory round trip per pass.
-                    constexpr int kC8 = kCols / 8;  // 8-column pieces of a block
-                    const int n_items = fz.T * kC8;
-                    for (int q0 = tid; q0 < n_items; q0 += 512) {
-                        uint64_t ov[2][8][4];
-                        float gv[2][8];
-                        int rr[2][8];
-                        uint4 rres[2];
-                        bool on[2];
-                        int64_t yo[2];
-#pragma unroll
-                        for (int it = 0; it < 2; ++it) {
-                            const int q = q0 + 256 * it;
-                            const int t = q / kC8;
-                            const int n = cb * kCols + (q - t * kC8) * 8;
-                            on[it] = q < n_items && n < N;
-                            const int tq = on[it] ? t : 0, nq = on[it] ? n : 0;
-                            yo[it] = (int64_t)tq * N + nq;
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) {
-                                if (j < fz.k) {
-                                    const int a = tq * fz.k + j;
-                                    const int r = s_map[a];
-                                    rr[it][j] = on[it] ? r : -1;
-                                    gv[it][j] = fz.gw[a];
-                                    // written by other workgroups in this launch:
-                                    // agent-coherent loads
-                                    const uint64_t *p =
-                                        (const uint64_t *)(out + (int64_t)max(r, 0) * N + nq);
-#pragma unroll
-                                    for (int c = 0; c < 4; ++c)
-                                        ov[it][j][c] = __hip_atomic_load(
-                                            p + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                                }
-                            }
-                            if (fz.residual) rres[it] = *(const uint4 *)(fz.residual + yo[it]);
-                        }
-#pragma unroll
-                        for (int it = 0; it < 2; ++it) {
-                            if (!on[it]) continue;
-                            float acc8[8];
-#pragma unroll
-                            for (int c = 0; c < 8; ++c) acc8[c] = 0.f;
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) {
-                                if (j < fz.k && rr[it][j] >= 0) {
-#pragma unroll
-                                    for (int c = 0; c < 4; ++c) {
-                                        const uint64_t v = ov[it][j][c];
-                                        acc8[2 * c] = fmaf(gv[it][j], __uint_as_float((uint32_t)v),
-                                                           acc8[2 * c]);
-                                        acc8[2 * c + 1] = fmaf(gv[it][j],
-                                                               __uint_as_float((uint32_t)(v >> 32)),
-                                                               acc8[2 * c + 1]);
-                                    }
-                                }
-                            }
-                            if (fz.residual) {
-                                const uint32_t w4[4] = {rres[it].x, rres[it].y, rres[it].z,
-                                                        rres[it].w};
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) {
-                                    acc8[2 * i] += bf16_bits_to_f32(w4[i] & 0xffffu);
-                                    acc8[2 * i + 1] += bf16_bits_to_f32(w4[i] >> 16);
-                                }
-                            }
-                            *(uint4 *)(fz.y + yo[it]) = make_uint4(
-                                pack_bf16x2(acc8[0], acc8[1]), pack_bf16x2(acc8[2], acc8[3]),
-                                pack_bf16x2(acc8[4], acc8[5]), pack_bf16x2(acc8[6], acc8[7]));
-                        }
-                    }
-                }
-                __syncthreads();
-            }
-        }
-    }
 }
 
 // The pieces of split tiles added in K order (so the sum is the same on
@@ -709,17 +594,6 @@ namespace {
 // Most pieces a tile may be split into (the kernel decides whether to split).
 constexpr int kSMaxPieces = 8;
 
-// In the decode layer: may the tiles be split?  At the smallest batches
-// (fewer than four rows per expert on average), and wherever GEMM2 cannot
-// have tiles for half the CUs (one or a few experts), since there whole
-// tiles leave CUs idle.  Elsewhere GEMM2 keeps whole tiles and forms y in
-// its own tail.
-int stream_layer_pieces(int64_t A, int d, int E) {
-    if (A <= 0) return 1;
-    const int64_t max_tiles2 = ((A + kSBT - 1) / kSBT + E - 1) * ((d + kSRowsT - 1) / kSRowsT);
-    return (A < 4 * (int64_t)E || 2 * max_tiles2 <= device_cus()) ? kSMaxPieces : 1;
-}
-
 // `reduce`: also launch the pass that sums split tiles' pieces (the decode
 // layer's GEMM2 leaves that to stream_reduce_combine_kernel).
 template <bool SWIGLU, typename TO>
@@ -764,41 +638,37 @@ bool stream_supported(int64_t A, int d, int d_ff, int E) {
            A <= kSMapMax && E <= 64;
 }
 
-int stream_combine_counters(int d) { return (d + kSRowsT - 1) / kSRowsT; }
 
 hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, const void *W2,
                                int64_t A, int d, int d_ff, int E, void *hbuf, float *out,
                                float *partial, size_t partial_bytes, const StreamFuse &fuse,
                                hipEvent_t gemm1_done, hipStream_t s) {
+    if (!fuse.y) return hipErrorInvalidValue;
     // one to eight tokens: each workgroup streams its own columns of every
     // active expert (stream_cols.hip), no split tiles, GEMM2 forms y
-    if (fuse.y && stream_cols_supported(fuse.T, fuse.k, d, d_ff, E))
+    if (stream_cols_supported(fuse.T, fuse.k, d, d_ff, E))
         return launch_stream_cols(x, W1, W3, W2, fuse.T, d, d_ff, E, hbuf, fuse, gemm1_done, s);
-    int pieces = stream_layer_pieces(A, d, E);
-    if (pieces > 1 && (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E))) pieces = 1;
+    // The tile kernels may always split: each launch takes the even K split
+    // when it cuts its busiest workgroup's K ranges by 10 % (few tiles, or a
+    // round a few tiles past the CUs when an expert needs a second token
+    // tile), and the pass after GEMM2 forms y from the pieces or the whole
+    // tiles' outputs.
+    if (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E)) return hipErrorInvalidValue;
     // nine to 32 tokens: GEMM2 on the column kernel, which forms y itself
-    const bool w2_cols = fuse.y && stream_cols_w2_supported(fuse.T, fuse.k, d, d_ff, E);
-    // GEMM1 reads token rows through the map it builds.  GEMM2 combines in
-    // its own tail where its tiles are never split (pieces == 1); else the pass
-    // that sums its pieces forms y.
+    const bool w2_cols = stream_cols_w2_supported(fuse.T, fuse.k, d, d_ff, E);
+    // GEMM1 reads token rows through the map it builds
     StreamFuse f1 = fuse;
-    f1.ctr_n = fuse.y && pieces == 1 && !w2_cols ? stream_combine_counters(d) : 0;
     f1.gw = nullptr;
     f1.residual = nullptr;
     f1.y = nullptr;
     hipError_t err = launch_stream<true, bf16_t>(x, d, fuse.token_of, W1, W3, fuse.offsets, E,
-                                                 d_ff, d, A, hbuf, pieces, partial, s, f1);
+                                                 d_ff, d, A, hbuf, kSMaxPieces, partial, s, f1);
     if (err == hipSuccess && gemm1_done) err = hipEventRecord(gemm1_done, s);
     if (err != hipSuccess) return err;
     if (w2_cols) return launch_stream_cols_w2(hbuf, W2, fuse.T, d, d_ff, E, fuse, s);
-    StreamFuse f2{};
-    if (pieces == 1 && fuse.y) {
-        f2 = fuse;
-        f2.topk_idx = nullptr;
-    }
     err = launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, fuse.offsets, E, d, d_ff,
-                                      A, out, pieces, partial, s, f2, !(pieces > 1 && fuse.y));
-    if (err != hipSuccess || pieces == 1 || !fuse.y) return err;
+                                      A, out, kSMaxPieces, partial, s, StreamFuse{}, false);
+    if (err != hipSuccess) return err;
     const int64_t T = fuse.T, n8 = T * d / 8;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n8 + 255) / 256));
     hipLaunchKernelGGL(stream_reduce_combine_kernel, dim3(grid), dim3(256), 0, s,

@@ -72,14 +72,14 @@ def test_permute_workspace_size_rules():
 
 def test_kernel_family_labels_follow_rows_per_expert():
     """The expert kernels are chosen by rows per expert (T k / E) on the host:
-    the weight stream below 25, grouped GEMM1 with wide GEMM2 below 49, the
+    the weight stream below 27, grouped GEMM1 with wide GEMM2 below 49, the
     wide kernels above (128-row token tiles up to 100, then 256), bf16 only
     for the stream and wide kernels; the grouped kernels take the rest
     (fp32, and d or d_ff too small for the wide tiles)."""
     f = lambda T, E=8, k=2, dt=moe.MOE_BF16, d=4096: moe.moe_expert_ffn_kernels(
         T, d, 14336, E, k, dt)
-    assert f(1) == f(99) == "stream_gemm_kernel"
-    assert f(100) == f(195) == ("grouped_gemm_kernel (128 x 64 tiles) + "
+    assert f(1) == f(107) == "stream_gemm_kernel"
+    assert f(108) == f(195) == ("grouped_gemm_kernel (128 x 64 tiles) + "
                                 "wide_gemm_kernel (128-row token tiles) (W2)")
     assert f(196) == "wide_gemm_kernel (128-row token tiles)"
     assert f(160, d=64).startswith("grouped_gemm_kernel (128 x 64")  # too small for wide
@@ -105,7 +105,7 @@ def test_layer_kernel_labels_name_the_column_kernels_up_to_eight_tokens():
         assert f(T) == "stream_cols_kernel" and g(T) == "stream_gemm_kernel"
     hybrid = "stream_gemm_kernel + stream_cols_kernel (W2)"   # GEMM1 tiles, GEMM2 columns
     assert f(9) == f(32) == hybrid and g(9) == g(32) == "stream_gemm_kernel"
-    assert f(33) == f(99) == "stream_gemm_kernel"
+    assert f(33) == f(107) == "stream_gemm_kernel"
     assert f(9, d=8192) == "stream_gemm_kernel"          # GEMM2: one column stage at most
     assert f(16, E=64, k=4) == hybrid and f(17, E=64, k=4) == "stream_gemm_kernel"  # 64 assignments
     assert f(100) == g(100) and f(4096) == g(4096)

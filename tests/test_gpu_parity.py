@@ -662,8 +662,8 @@ MIXED = "grouped_gemm_kernel (128 x 64 tiles) + wide_gemm_kernel (128-row token 
 
 
 @pytest.mark.parametrize("T,family", [
-    (99, "stream_gemm_kernel"),                      # 24 rows per expert on average
-    (100, MIXED),                                    # 25
+    (107, "stream_gemm_kernel"),                     # 26 rows per expert on average
+    (108, MIXED),                                    # 27
     (195, MIXED),                                    # 48
     (196, "wide_gemm_kernel (128-row token tiles)"),  # 49
     (400, "wide_gemm_kernel (128-row token tiles)"),  # 100
