@@ -157,7 +157,7 @@ moe_status moe_permute(const void *x, const int32_t *topk_idx, moe_dtype dt, int
  * produced by moe_permute; offsets[E] <= T*k).  Rows at or beyond offsets[E]
  * are left untouched.  ws holds the SwiGLU intermediate (rows x d_ff) and,
  * for large bf16 batches and for decode-sized ones (the weight-streaming
- * kernels, up to 24 rows per expert), fp32 partial sums of tiles split along
+ * kernels, up to 26 rows per expert), fp32 partial sums of tiles split along
  * K where whole tiles would leave CUs idle (summed in a fixed order: results
  * are deterministic); moe_workspace_size() bytes always suffice.
  * Defined by: fdeinterviews breakdown, "The paper in one minute" (the experts
