@@ -595,12 +595,14 @@ namespace {
 constexpr int kSMaxPieces = 8;
 
 // `reduce`: also launch the pass that sums split tiles' pieces (the decode
-// layer's GEMM2 leaves that to stream_reduce_combine_kernel).
+// layer's GEMM2 leaves that to stream_reduce_combine_kernel).  `after`, if
+// set, is recorded right after the GEMM kernel, before that pass.
 template <bool SWIGLU, typename TO>
 hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
                          void *out, int max_pieces, float *part, hipStream_t s,
-                         const StreamFuse &fz = StreamFuse{}, bool reduce = true) {
+                         const StreamFuse &fz = StreamFuse{}, bool reduce = true,
+                         hipEvent_t after = nullptr) {
     hipError_t err = set_lds_limit<stream_gemm_kernel<SWIGLU, TO>>(kSLds);
     if (err != hipSuccess) return err;
     // one workgroup per CU, never more than there can be items:
@@ -611,7 +613,9 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather,
     hipLaunchKernelGGL((stream_gemm_kernel<SWIGLU, TO>), dim3(grid), dim3(256), kSLds, s,
                        (const bf16_t *)act, act_ld, gather, (const bf16_t *)Wa,
                        (const bf16_t *)Wb, offsets, E, N, K, (int)A, (TO *)out, max_pieces, part, fz);
-    if ((err = hipGetLastError()) != hipSuccess || max_pieces == 1 || !reduce) return err;
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (after && (err = hipEventRecord(after, s)) != hipSuccess) return err;
+    if (max_pieces == 1 || !reduce) return err;
     const int64_t n4 = A * N / 4;  // N is a multiple of 512
     const int rgrid = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (n4 + 255) / 256));
     hipLaunchKernelGGL((stream_reduce_kernel<SWIGLU, TO>), dim3(rgrid), dim3(256), 0, s,
@@ -662,8 +666,8 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
     f1.residual = nullptr;
     f1.y = nullptr;
     hipError_t err = launch_stream<true, bf16_t>(x, d, fuse.token_of, W1, W3, fuse.offsets, E,
-                                                 d_ff, d, A, hbuf, kSMaxPieces, partial, s, f1);
-    if (err == hipSuccess && gemm1_done) err = hipEventRecord(gemm1_done, s);
+                                                 d_ff, d, A, hbuf, kSMaxPieces, partial, s, f1,
+                                                 true, gemm1_done);
     if (err != hipSuccess) return err;
     if (w2_cols) return launch_stream_cols_w2(hbuf, W2, fuse.T, d, d_ff, E, fuse, s);
     err = launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, fuse.offsets, E, d, d_ff,
@@ -686,8 +690,8 @@ hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32
     int pieces = kSMaxPieces;
     if (!partial || partial_bytes < stream_partial_bytes(A, d, d_ff, E)) pieces = 1;
     hipError_t err = launch_stream<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A,
-                                                 hbuf, pieces, partial, s);
-    if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
+                                                 hbuf, pieces, partial, s, StreamFuse{}, true,
+                                                 mid);
     if (err != hipSuccess) return err;
     if (out_f32)
         return launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff,

@@ -527,10 +527,11 @@ namespace {
 // one workgroup per CU, a multiple of 8 (one share per XCD), at most 64 per XCD
 int wide_grid() { return std::max(8, std::min(device_cus(), 512) / 8 * 8); }
 
+// `after`, if set, is recorded right after the GEMM kernel, before the fixup.
 template <bool SWIGLU, typename TO, int BT>
 hipError_t launch_wide_bt(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                           const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
-                          void *out, float *partial, hipStream_t s) {
+                          void *out, float *partial, hipStream_t s, hipEvent_t after) {
     using C = WideTile<BT>;
     auto kern = wide_gemm_kernel<SWIGLU, TO, BT>;
     hipError_t err = set_lds_limit<wide_gemm_kernel<SWIGLU, TO, BT>>(C::kLds);
@@ -539,7 +540,9 @@ hipError_t launch_wide_bt(const void *act, int64_t act_ld, const int32_t *gather
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), C::kLds, s, (const bf16_t *)act, act_ld,
                        gather, (const bf16_t *)Wa, (const bf16_t *)Wb, offsets, E, N, K, (int)A,
                        (TO *)out, partial);
-    if ((err = hipGetLastError()) != hipSuccess || !partial) return err;
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (after && (err = hipEventRecord(after, s)) != hipSuccess) return err;
+    if (!partial) return err;
     hipLaunchKernelGGL((wide_fixup_kernel<SWIGLU, TO, BT>), dim3(grid * (C::kFW / 4)), dim3(256),
                        0, s, offsets, E, N, K, (int)A, grid / 8, (TO *)out,
                        (const float *)partial);
@@ -552,12 +555,12 @@ hipError_t launch_wide_bt(const void *act, int64_t act_ld, const int32_t *gather
 template <bool SWIGLU, typename TO>
 hipError_t launch_wide(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                        const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
-                       void *out, float *partial, hipStream_t s) {
+                       void *out, float *partial, hipStream_t s, hipEvent_t after = nullptr) {
     if (wide_token_tile(A, E) == 128)
         return launch_wide_bt<SWIGLU, TO, 128>(act, act_ld, gather, Wa, Wb, offsets, E, N, K, A,
-                                               out, partial, s);
+                                               out, partial, s, after);
     return launch_wide_bt<SWIGLU, TO, 256>(act, act_ld, gather, Wa, Wb, offsets, E, N, K, A, out,
-                                           partial, s);
+                                           partial, s, after);
 }
 
 }  // namespace
@@ -584,8 +587,7 @@ hipError_t launch_wide_ffn(const void *act, const int32_t *gather, const int32_t
                            size_t partial_bytes, hipEvent_t mid, hipStream_t s) {
     if (partial && partial_bytes < wide_partial_bytes(A, E)) partial = nullptr;  // no splits
     hipError_t err = launch_wide<true, bf16_t>(act, d, gather, W1, W3, offsets, E, d_ff, d, A,
-                                               hbuf, partial, s);
-    if (err == hipSuccess && mid) err = hipEventRecord(mid, s);
+                                               hbuf, partial, s, mid);
     if (err != hipSuccess) return err;
     if (out_f32)
         return launch_wide<false, float>(hbuf, d_ff, nullptr, W2, nullptr, offsets, E, d, d_ff,

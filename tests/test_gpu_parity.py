@@ -455,6 +455,34 @@ def test_side_streams_give_the_default_streams_result(name):
         assert torch.equal(y, y0)
 
 
+@pytest.mark.parametrize("name", ["tiny", "stream-tiles", "split-9-tokens", "cols-three-tokens",
+                                  "grouped-bf16", "mixed-mid", "wide-narrow", "wide-many"])
+def test_profiled_layer_is_the_layer(name):
+    """moe_forward_profiled, with all six stage events or only GEMM1's pair,
+    gives moe_forward's output bit for bit, and its events are recorded in
+    stage order on the launch stream (every elapsed time between consecutive
+    ones is >= 0, GEMM1's > 0)."""
+    import bench
+    w = next(v for v in SMALL if v.name == name)
+    L = _case(w)
+    y0 = moe.moe_forward(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.k)
+    ev = bench.HipEvents()
+    e = [ev.create() for _ in range(6)]
+    y1 = moe.moe_forward_profiled(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.k, e)
+    torch.cuda.synchronize()
+    gaps = [ev.elapsed_ms(e[i], e[i + 1]) for i in range(5)]
+    g = [ev.create(), ev.create()]
+    y2 = moe.moe_forward_profiled(L["x"], L["Wg"], L["W1"], L["W3"], L["W2"], w.k,
+                                  [None, None, g[0], g[1], None, None])
+    torch.cuda.synchronize()
+    g1 = ev.elapsed_ms(g[0], g[1])
+    for h in e + g:
+        ev.destroy(h)
+    log(f"  stage ms {[round(v, 4) for v in gaps]}, GEMM1 alone {g1:.4f}")
+    assert torch.equal(y1, y0) and torch.equal(y2, y0)
+    assert min(gaps) >= 0.0 and gaps[2] > 0.0 and g1 > 0.0
+
+
 @pytest.mark.parametrize("name", ["stream-tiles", "split-9-tokens", "cols-three-tokens",
                                   "cols-eight-tokens", "grouped-bf16", "wide-narrow"])
 def test_layer_replays_from_a_hip_graph(name):
