@@ -210,8 +210,8 @@ moe_status moe_forward_noalloc(const void *x, const float *Wg, const void *W1, c
  * between events[i] and events[i+1] is stage i's device time.  events[3] is
  * recorded right after the GEMM1 kernel itself, so events[2]..events[3]
  * bracket that one kernel; a pass that completes GEMM1's K-split tiles
- * (weight-stream and wide kernels) counts to stage 3.  Otherwise identical
- * to moe_forward. */
+ * (the wide kernels' fixup) counts to stage 3.  Otherwise identical to
+ * moe_forward. */
 moe_status moe_forward_profiled(const void *x, const float *Wg, const void *W1, const void *W3,
                                 const void *W2, moe_dtype dt, int64_t T, int d, int d_ff, int E,
                                 int k, void *y, void *ws, size_t ws_bytes, void *const *events,

@@ -290,10 +290,18 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
     auto mark = [&](int i) -> hipError_t {
         return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
     };
+    // Decode sizes on the weight-streaming tile kernels: GEMM1 finishes its
+    // K-split tiles itself, with one counter per tile that the router zeroes.
+    const bool streams = moe_expert_ffn_streams((int)dt, A, d, d_ff, E);
+    const int n_ctr =
+        streams && c.split_bytes ? moe_stream_layer_counters((int)dt, T, k, d, d_ff, E) : 0;
+    int32_t *ctr = n_ctr ? at<int32_t>(ws, c.split) + moe_stream_layer_counter_index(T, k, d, d_ff)
+                         : nullptr;
     LAUNCH(mark(0), "event");
-    LAUNCH(moe_launch_router(x, (int)dt, Wg, T, d, E, k, idx, gw, nullptr, s), "router");
+    LAUNCH(moe_launch_router(x, (int)dt, Wg, T, d, E, k, idx, gw, nullptr, s, ctr, n_ctr),
+           "router");
     LAUNCH(mark(1), "event");
-    if (moe_expert_ffn_streams((int)dt, A, d, d_ff, E)) {
+    if (streams) {
         // Decode sizes: the weight-streaming GEMM1 groups the assignments
         // itself, and GEMM2 or the pass after it also combines (dispatch and
         // combine stages empty).
@@ -302,7 +310,7 @@ static moe_status forward_impl(const void *x, const float *Wg, const void *W1, c
                                        offsets, row_of, token_of, hbuf,
                                        (float *)o_perm, y,
                                        c.split_bytes ? at<char>(ws, c.split) : nullptr,
-                                       c.split_bytes, ev ? (hipEvent_t)ev[3] : nullptr, s),
+                                       c.split_bytes, ctr, ev ? (hipEvent_t)ev[3] : nullptr, s),
                "expert_ffn");
         LAUNCH(mark(4), "event");
         LAUNCH(mark(5), "event");

@@ -59,8 +59,11 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double v) {
 
 // ---- launchers (host side, one per kernel family) -------------------------
 
+// zero [zero_n] (may be NULL): int32 counters that workgroup 0 of the router
+// sets to 0, for the launch after it.
 hipError_t moe_launch_router(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
-                             int k, int32_t *idx, float *gw, float *logits, hipStream_t s);
+                             int k, int32_t *idx, float *gw, float *logits, hipStream_t s,
+                             int32_t *zero = nullptr, int zero_n = 0);
 // Workgroups of the router launch for T tokens (one statistics row each).
 int64_t moe_router_blocks(int64_t T);
 // Router plus load statistics: part_p [blocks][E] fp64 and part_c [blocks][E]
@@ -100,13 +103,20 @@ size_t moe_expert_ffn_scratch_bytes(int dt, int64_t A, int d, int d_ff, int E);
 // (bf16; o_perm fp32 in between).  scratch: at least
 // moe_expert_ffn_scratch_bytes() of the shape (the split-tile scratch).
 bool moe_expert_ffn_streams(int dt, int64_t A, int d, int d_ff, int E);
+// `ctr` [moe_stream_layer_counters()] (may be NULL when that is 0): counters
+// zeroed by an earlier launch on the stream (the router's), with which GEMM1
+// finishes its own K-split tiles; NULL: a pass after GEMM1 does.
 hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k, const float *gw,
                                    const void *residual, const void *W1, const void *W3,
                                    const void *W2, int64_t T, int d, int d_ff, int E,
                                    int32_t *counts, int32_t *offsets, int32_t *row_of,
                                    int32_t *token_of, void *hbuf, float *o_perm, void *y,
-                                   void *scratch, size_t scratch_bytes, hipEvent_t gemm1_done,
-                                   hipStream_t s);
+                                   void *scratch, size_t scratch_bytes, int32_t *ctr,
+                                   hipEvent_t gemm1_done, hipStream_t s);
+// Counters of the layer's GEMM1 at T tokens (0 where its GEMM1 is not the
+// tile kernel) and where they sit in the split-tile scratch (int32 index).
+int moe_stream_layer_counters(int dt, int64_t T, int k, int d, int d_ff, int E);
+int64_t moe_stream_layer_counter_index(int64_t T, int k, int d, int d_ff);
 // Name of the kernel family that runs the experts for this shape.
 const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E);
 // The same for the experts of the fused layer (moe_forward and friends) at T

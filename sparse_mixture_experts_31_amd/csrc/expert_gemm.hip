@@ -384,10 +384,11 @@ hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k
                                    const void *W2, int64_t T, int d, int d_ff, int E,
                                    int32_t *counts, int32_t *offsets, int32_t *row_of,
                                    int32_t *token_of, void *hbuf, float *o_perm, void *y,
-                                   void *scratch, size_t scratch_bytes, hipEvent_t gemm1_done,
-                                   hipStream_t s) {
+                                   void *scratch, size_t scratch_bytes, int32_t *ctr,
+                                   hipEvent_t gemm1_done, hipStream_t s) {
     const int64_t A = T * k;
     moe::StreamFuse f{};
+    f.ctr = ctr;
     f.topk_idx = topk_idx;
     f.k = k;
     f.counts = counts;
@@ -400,6 +401,17 @@ hipError_t moe_launch_stream_layer(const void *x, const int32_t *topk_idx, int k
     f.T = (int)T;
     return moe::launch_stream_fused(x, W1, W3, W2, A, d, d_ff, E, hbuf, o_perm, (float *)scratch,
                                     scratch_bytes, f, gemm1_done, s);
+}
+
+int moe_stream_layer_counters(int dt, int64_t T, int k, int d, int d_ff, int E) {
+    if (!moe_expert_ffn_streams(dt, T * k, d, d_ff, E) ||
+        moe::stream_cols_supported(T, k, d, d_ff, E))
+        return 0;
+    return (int)moe::stream_gemm1_tiles_max(T * k, d_ff, E);
+}
+
+int64_t moe_stream_layer_counter_index(int64_t T, int k, int d, int d_ff) {
+    return moe::stream_counter_index(T * k, d, d_ff);
 }
 
 const char *moe_expert_ffn_kernel_name(int dt, int64_t A, int d, int d_ff, int E) {

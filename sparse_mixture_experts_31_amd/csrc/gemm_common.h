@@ -229,6 +229,10 @@ struct StreamFuse {
     const bf16_t *residual;
     bf16_t *y;
     int T;
+    // GEMM1 of the layer: one counter per tile, zero at the launch; the
+    // pieces of split tiles are written through to memory and the last
+    // workgroup to count a tile's piece sums them (no pass after GEMM1).
+    int32_t *ctr;
 };
 
 // Weight-streaming expert GEMMs for decode-sized bf16 batches
@@ -237,6 +241,10 @@ struct StreamFuse {
 // smallest batches, at least stream_partial_bytes() bytes (0: none used).
 bool stream_supported(int64_t A, int d, int d_ff, int E);
 size_t stream_partial_bytes(int64_t A, int d, int d_ff, int E);
+// The layer GEMM1's counters (one per tile, stream_gemm1_tiles_max of them)
+// start at int32 index stream_counter_index() of that scratch.
+int64_t stream_gemm1_tiles_max(int64_t A, int d_ff, int E);
+int64_t stream_counter_index(int64_t A, int d, int d_ff);
 hipError_t launch_stream_ffn(const void *act, const int32_t *gather, const int32_t *offsets,
                              const void *W1, const void *W3, const void *W2, int out_f32,
                              int64_t A, int d, int d_ff, int E, void *hbuf, void *out,

@@ -122,7 +122,11 @@ template <typename Tin, int TPW, int EG, int WPT, bool STATS = false, int WAVES 
 __global__ __launch_bounds__(WAVES * kWave) void router_topk_kernel(
     const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,
     int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits,
-    double *__restrict__ part_p = nullptr, int32_t *__restrict__ part_c = nullptr) {
+    double *__restrict__ part_p = nullptr, int32_t *__restrict__ part_c = nullptr,
+    int32_t *__restrict__ zero = nullptr, int zero_n = 0) {
+    // zero[0, zero_n): counters the launch after this one starts from
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < zero_n; i += WAVES * kWave) zero[i] = 0;
     constexpr int kGroups = WAVES / WPT;  // token groups per workgroup
     __shared__ float s_logit[kGroups][TPW][64];
     __shared__ double s_part[kGroups][WPT][TPW * EG];
@@ -246,8 +250,12 @@ constexpr int kRouterLdsBytes = 128 * 1024;  // most Wg bytes held in LDS
 template <typename Tin, int TPW>
 __global__ __launch_bounds__(kRouterLdsWaves * kWave) void router_topk_lds_kernel(
     const Tin *__restrict__ x, const float *__restrict__ Wg, int64_t T, int d, int E, int k,
-    int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits) {
+    int32_t *__restrict__ out_idx, float *__restrict__ out_w, float *__restrict__ out_logits,
+    int32_t *__restrict__ zero, int zero_n) {
     extern __shared__ __attribute__((aligned(16))) float s_wg[];  // [E][d]
+    // zero[0, zero_n): counters the launch after this one starts from
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < zero_n; i += kRouterLdsWaves * kWave) zero[i] = 0;
     __shared__ float s_logit[kRouterLdsWaves][TPW][64];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -387,7 +395,8 @@ bool router_wide_rows(int64_t T) { return T < 1024; }
 
 template <typename Tin, int TPW>
 hipError_t launch_router_lds_t(const Tin *x, const float *Wg, int64_t T, int d, int E, int k,
-                               int32_t *idx, float *gw, float *logits, hipStream_t s) {
+                               int32_t *idx, float *gw, float *logits, int32_t *zero, int zero_n,
+                               hipStream_t s) {
     using namespace moe;
     const int bytes = E * d * (int)sizeof(float);  // <= kRouterLdsBytes
     hipError_t err = set_lds_limit<router_topk_lds_kernel<Tin, TPW>>(kRouterLdsBytes);
@@ -396,7 +405,7 @@ hipError_t launch_router_lds_t(const Tin *x, const float *Wg, int64_t T, int d, 
     const int64_t blocks = std::min<int64_t>(device_cus(), (T + per_block - 1) / per_block);
     hipLaunchKernelGGL((router_topk_lds_kernel<Tin, TPW>), dim3((unsigned)blocks),
                        dim3(kRouterLdsWaves * kWave), bytes, s, x, Wg, T, d, E, k, idx, gw,
-                       logits);
+                       logits, zero, zero_n);
     return hipGetLastError();
 }
 
@@ -405,41 +414,48 @@ hipError_t launch_router_lds_t(const Tin *x, const float *Wg, int64_t T, int d, 
 // and the T = 16384 one from 99 to 87 us; four were eight times slower.)
 template <typename Tin>
 hipError_t launch_router_lds(const Tin *x, const float *Wg, int64_t T, int d, int E, int k,
-                             int32_t *idx, float *gw, float *logits, hipStream_t s) {
+                             int32_t *idx, float *gw, float *logits, int32_t *zero, int zero_n,
+                             hipStream_t s) {
     const int64_t full = (int64_t)moe::kRouterLdsWaves * moe::device_cus();  // waves in one pass
     if (T >= 2 * full)
-        return launch_router_lds_t<Tin, 2>(x, Wg, T, d, E, k, idx, gw, logits, s);
-    return launch_router_lds_t<Tin, 1>(x, Wg, T, d, E, k, idx, gw, logits, s);
+        return launch_router_lds_t<Tin, 2>(x, Wg, T, d, E, k, idx, gw, logits, zero, zero_n, s);
+    return launch_router_lds_t<Tin, 1>(x, Wg, T, d, E, k, idx, gw, logits, zero, zero_n, s);
 }
 
 template <bool STATS>
 hipError_t launch_router_impl(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
                               int k, int32_t *idx, float *gw, float *logits, double *part_p,
-                              int32_t *part_c, hipStream_t s) {
+                              int32_t *part_c, hipStream_t s, int32_t *zero = nullptr,
+                              int zero_n = 0) {
     using namespace moe;
     const dim3 block(kRouterWaves * kWave);
     const dim3 grid((unsigned)moe_router_blocks(T));
     if (!STATS && !router_wide_rows(T) && d % 512 == 0 && (int64_t)E * d * 4 <= kRouterLdsBytes) {
         // many tokens, Wg small enough for LDS
-        if (dt == 0) return launch_router_lds((const float *)x, Wg, T, d, E, k, idx, gw, logits, s);
-        return launch_router_lds((const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, s);
+        if (dt == 0)
+            return launch_router_lds((const float *)x, Wg, T, d, E, k, idx, gw, logits, zero,
+                                     zero_n, s);
+        return launch_router_lds((const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, zero, zero_n,
+                                 s);
     }
     if (router_wide_rows(T)) {
         if (dt == 0)
             hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 4, STATS>), grid, block, 0, s,
-                               (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p, part_c);
+                               (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p, part_c,
+                               zero, zero_n);
         else
             hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 4, STATS>), grid, block, 0, s,
                                (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, part_p,
-                               part_c);
+                               part_c, zero, zero_n);
     } else {
         if (dt == 0)
             hipLaunchKernelGGL((router_topk_kernel<float, 1, 8, 1, STATS>), grid, block, 0, s,
-                               (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p, part_c);
+                               (const float *)x, Wg, T, d, E, k, idx, gw, logits, part_p, part_c,
+                               zero, zero_n);
         else
             hipLaunchKernelGGL((router_topk_kernel<bf16_t, 1, 8, 1, STATS>), grid, block, 0, s,
                                (const bf16_t *)x, Wg, T, d, E, k, idx, gw, logits, part_p,
-                               part_c);
+                               part_c, zero, zero_n);
     }
     return hipGetLastError();
 }
@@ -451,9 +467,10 @@ int64_t moe_router_blocks(int64_t T) {
 }
 
 hipError_t moe_launch_router(const void *x, int dt, const float *Wg, int64_t T, int d, int E,
-                             int k, int32_t *idx, float *gw, float *logits, hipStream_t s) {
+                             int k, int32_t *idx, float *gw, float *logits, hipStream_t s,
+                             int32_t *zero, int zero_n) {
     return launch_router_impl<false>(x, dt, Wg, T, d, E, k, idx, gw, logits, nullptr, nullptr,
-                                     s);
+                                     s, zero, zero_n);
 }
 
 hipError_t moe_launch_route_balance(const void *x, int dt, const float *Wg, int64_t T, int d,

@@ -57,6 +57,30 @@ static_assert(kSLds <= 160 * 1024 - 3 * 1024, "LDS capacity (3 KiB of static tab
 static_assert(kSGrp == 16 && kSGroups == 8, "one 16-row MFMA fragment per stage, 8 per K range");
 static_assert(kSP - 1 <= kSGroups / 2, "prologue stages carry no token loads");
 
+// Four fp32 partial sums of a split tile's piece, as two 64-bit stores:
+// written through to memory when another workgroup of the same launch will
+// read them (agent-coherent), else plain.
+__device__ __forceinline__ void put_piece(float *p, const f32x4 &v, bool coherent) {
+    if (coherent) {
+        uint64_t *q = (uint64_t *)p;
+        __hip_atomic_store(q, ((uint64_t)__float_as_uint(v[1]) << 32) | __float_as_uint(v[0]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 1, ((uint64_t)__float_as_uint(v[3]) << 32) | __float_as_uint(v[2]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        *(f32x4 *)p = v;
+    }
+}
+
+// A piece written by another workgroup of this launch (agent-coherent loads).
+__device__ __forceinline__ f32x4 get_piece(const float *p) {
+    const uint64_t *q = (const uint64_t *)p;
+    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                 __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+
 // Loads a wave issues along with stage row group rg: 4 weight rows, and in
 // the second half of a K range 2 token rows of the next one.
 constexpr int loads_of(int rg) { return 4 + (rg >= kSGroups / 2 ? 2 : 0); }
@@ -450,7 +474,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 np = wg_of(cit.t * n_kr + n_kr - 1) - first + 1;
             }
             const int slot = 2 * (int)blockIdx.x + (ck == 0 ? 0 : 1);
-            if (split && first == (int)blockIdx.x && par == 0 && lq == 0)
+            if (split && !fz.ctr && first == (int)blockIdx.x && par == 0 && lq == 0)
                 info[row * col_tiles + cti.n0 / kCols] = m | (np << 5) | (slot << 9);
 #pragma unroll
             for (int h = 0; h < (SWIGLU ? 2 : 4); ++h) {
@@ -459,8 +483,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (n < N) {
                     if (np > 1) {
                         float *sl = slots + (int64_t)slot * kSSlot + m * kSRowsT + c;
-                        *(f32x4 *)sl = acc[h];
-                        if constexpr (SWIGLU) *(f32x4 *)(sl + kSRowsT / 2) = acc[h + 2];
+                        put_piece(sl, acc[h], fz.ctr != nullptr);
+                        if constexpr (SWIGLU)
+                            put_piece(sl + kSRowsT / 2, acc[h + 2], fz.ctr != nullptr);
                     } else {
                         float r[4];
 #pragma unroll
@@ -477,6 +502,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = 0; i < 4; ++i) acc[i] = f32x4{};
     }
     wait_vmcnt_lgkm0<0>();  // the trailing reloads land before the wave ends
+
+    // With counters (the layer's GEMM1) the kernel finishes its split tiles
+    // itself.  Only a workgroup's first and last items can be pieces; once
+    // every wave's stores are done (the wait above) it counts each of them
+    // on its tile, and the workgroup that completes a tile's count adds the
+    // pieces in K order and applies the epilogue, as stream_reduce_kernel
+    // does (the same sums in the same order).  The pieces were written
+    // through to memory and are read with agent-coherent loads: no cache
+    // flush or invalidation, which would stall the XCD's workgroups still
+    // streaming.
+    if (split && fz.ctr) {
+        __shared__ int s_last;
+        constexpr int kC4 = kCols / 4;
+        for (int j = 0; j < 2 && j < my_items; ++j) {
+            const Item it = item_info(j == 0 ? 0 : my_items - 1);
+            const int first = wg_of(it.t * n_kr);
+            const int np = wg_of(it.t * n_kr + n_kr - 1) - first + 1;
+            if (np <= 1) continue;  // a whole tile, stored above
+            __syncthreads();        // s_last of the previous tile has been read
+            if (tid == 0)
+                s_last = __hip_atomic_fetch_add(&fz.ctr[it.t], 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+            __syncthreads();
+            if (!s_last) continue;
+            // piece 0 is workgroup `first`'s last item, or its first if the
+            // tile is where its ranges start; piece p > 0 is the first item
+            // of workgroup first + p
+            const int t_of_first = (int)(((int64_t)first * R / NGe) / n_kr);
+            const int s0 = 2 * first + (t_of_first == it.t ? 0 : 1);
+            for (int q = tid; q < kSBT * kC4; q += 256) {
+                const int m = q / kC4, c = (q - m * kC4) * 4;
+                const int n = it.ti.n0 + c;
+                if (m >= it.ti.mrem || n >= N) continue;
+                const float *p0 = slots + (int64_t)s0 * kSSlot + m * kSRowsT + c;
+                f32x4 uu = get_piece(p0), vv = {};
+                if constexpr (SWIGLU) vv = get_piece(p0 + kSRowsT / 2);
+                for (int pc = 1; pc < np; ++pc) {
+                    const float *pq = slots + (int64_t)(2 * (first + pc)) * kSSlot + m * kSRowsT + c;
+                    uu += get_piece(pq);
+                    if constexpr (SWIGLU) vv += get_piece(pq + kSRowsT / 2);
+                }
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = SWIGLU ? silu(uu[i]) * vv[i] : uu[i];
+                store4<TO>(out + (int64_t)(it.ti.row0 + m) * N + n, o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
 }
 
 // The pieces of split tiles added in K order (so the sum is the same on
@@ -625,15 +698,28 @@ hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather,
 
 }  // namespace
 
+// GEMM1's tiles at most (one counter each when the layer's GEMM1 finishes its
+// own split tiles): ceil(c_e / BT) token tiles per expert sum to at most
+// ceil(A / BT) + E - 1.
+int64_t stream_gemm1_tiles_max(int64_t A, int d_ff, int E) {
+    const int64_t cols = (d_ff + kSRowsT / 2 - 1) / (kSRowsT / 2);
+    return cols * ((std::max<int64_t>(A, 0) + kSBT - 1) / kSBT + E - 1);
+}
+
+// int32 index in the split scratch where those counters start: past the
+// header, two slots per workgroup (at most one per CU) and the tile
+// description per row and column tile (the larger of GEMM1's and GEMM2's;
+// the two launches run one after the other).
+int64_t stream_counter_index(int64_t A, int d, int d_ff) {
+    const int64_t col_tiles = std::max((d_ff + kSRowsT / 2 - 1) / (kSRowsT / 2),
+                                       (d + kSRowsT - 1) / kSRowsT);
+    return (int64_t)kSPartHdr + (int64_t)2 * device_cus() * kSSlot +
+           std::max<int64_t>(A, 0) * col_tiles;
+}
+
 size_t stream_partial_bytes(int64_t A, int d, int d_ff, int E) {
-    // header + two slots per workgroup (at most one per CU) + the tile
-    // description per row and column tile (the larger of GEMM1's and
-    // GEMM2's); the two launches run one after the other
-    (void)E;
-    const size_t col_tiles = std::max((d_ff + kSRowsT / 2 - 1) / (kSRowsT / 2),
-                                      (d + kSRowsT - 1) / kSRowsT);
-    return sizeof(float) * ((size_t)kSPartHdr + (size_t)2 * device_cus() * kSSlot) +
-           sizeof(int32_t) * (size_t)std::max<int64_t>(A, 0) * col_tiles;
+    return sizeof(int32_t) *
+           (size_t)(stream_counter_index(A, d, d_ff) + stream_gemm1_tiles_max(A, d_ff, E));
 }
 
 bool stream_supported(int64_t A, int d, int d_ff, int E) {
@@ -665,9 +751,10 @@ hipError_t launch_stream_fused(const void *x, const void *W1, const void *W3, co
     f1.gw = nullptr;
     f1.residual = nullptr;
     f1.y = nullptr;
+    // with counters GEMM1 finishes its split tiles itself (no pass after it)
     hipError_t err = launch_stream<true, bf16_t>(x, d, fuse.token_of, W1, W3, fuse.offsets, E,
                                                  d_ff, d, A, hbuf, kSMaxPieces, partial, s, f1,
-                                                 true, gemm1_done);
+                                                 fuse.ctr == nullptr, gemm1_done);
     if (err != hipSuccess) return err;
     if (w2_cols) return launch_stream_cols_w2(hbuf, W2, fuse.T, d, d_ff, E, fuse, s);
     err = launch_stream<false, float>(hbuf, d_ff, nullptr, W2, nullptr, fuse.offsets, E, d, d_ff,
