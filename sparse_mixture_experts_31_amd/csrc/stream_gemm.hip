@@ -668,8 +668,9 @@ namespace {
 constexpr int kSMaxPieces = 8;
 
 // `reduce`: also launch the pass that sums split tiles' pieces (the decode
-// layer's GEMM2 leaves that to stream_reduce_combine_kernel).  `after`, if
-// set, is recorded right after the GEMM kernel, before that pass.
+// layer's GEMM1 sums them itself, with counters, and its GEMM2 leaves that
+// to stream_reduce_combine_kernel).  `after`, if set, is recorded right
+// after the GEMM kernel, before that pass.
 template <bool SWIGLU, typename TO>
 hipError_t launch_stream(const void *act, int64_t act_ld, const int32_t *gather, const void *Wa,
                          const void *Wb, const int32_t *offsets, int E, int N, int K, int64_t A,
