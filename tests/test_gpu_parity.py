@@ -863,7 +863,7 @@ def _random_workload(seed):
     return Workload(f"random-{seed}", 200 + seed, T=T, d=d, d_ff=d_ff, E=E, k=k, dtype=dt)
 
 
-@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_shapes(seed):
     """moe_forward on seeded random shapes (every kernel family and their
     thresholds) against the oracle on up to 48 sampled tokens."""
@@ -871,3 +871,21 @@ def test_random_shapes(seed):
     L = _case(w)
     rows = None if w.T <= 48 else np.sort(np.random.default_rng(seed).choice(w.T, 48, replace=False))
     _forward_and_check(w, L, rows=rows)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_tile_stream_shapes(seed):
+    """9 to 32 tokens on weight-stream shapes (d, d_ff multiples of 512): the
+    layer's GEMM1 on the tile kernel, which sums the pieces of the tiles it
+    splits itself (the last workgroup to count a tile's piece), and GEMM2 on
+    the column kernel; random E and k, every token checked against the
+    oracle."""
+    rng = np.random.default_rng(5000 + seed)
+    E = int(rng.choice([2, 4, 8, 8, 16, 64]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(9, 33))
+    k = min(k, 64 // T)
+    w = Workload(f"tile-stream-{seed}", 300 + seed, T=T, d=int(rng.choice([512, 1024, 2048])),
+                 d_ff=int(rng.choice([512, 1024, 1536, 2048, 3584])), E=E, k=k)
+    L = _case(w)
+    _forward_and_check(w, L)
